@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the attention arithmetic. Both the GPU library's tests/bench and
+the CPU oracle consume what it returns, so the two sides always see the same
+input values.
+
+Recipe: i.i.d. standard normals from NumPy's PCG64 generator in float32, drawn
+in the order Q, K, V, dO, then rounded to the workload dtype (bf16 by
+round-to-nearest-even via torch on the CPU). A query multiplier (a power of
+two, so exact in bf16) widens the score range for the softmax-stress workload.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "bf16" or "f32"
+    causal: bool
+    dropout_p: float = 0.0
+    q_mult: float = 1.0
+    backward: bool = False
+    data_seed: int = 0
+    row_seed: int = 0     # seeds the sample of query rows checked at full size
+    head_seed: int = 0    # seeds the sample of heads checked at full size
+    dropout_seed: int = 0x0123456789ABCDEF
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.d))
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def fwd_flops(self) -> float:
+        """Counted forward FLOPs: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """Counted backward FLOPs: 2.5x the forward count (five products against two)."""
+        return 2.5 * self.fwd_flops()
+
+
+# The five workloads the library is specified on; named by what they are.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("fwd_f32_b1h1n128d64", 1, 1, 128, 64, "f32", causal=False,
+                 data_seed=1001, row_seed=2001, head_seed=3001),
+        Workload("fwd_causal_bf16_b4h16n2048d64", 4, 16, 2048, 64, "bf16", causal=True,
+                 data_seed=1002, row_seed=2002, head_seed=3002),
+        Workload("fwd_causal_q4_bf16_b2h32n8192d128", 2, 32, 8192, 128, "bf16", causal=True,
+                 q_mult=4.0, data_seed=1003, row_seed=2003, head_seed=3003),
+        Workload("fwdbwd_causal_dropout_bf16_b2h16n4096d64", 2, 16, 4096, 64, "bf16",
+                 causal=True, dropout_p=0.1, backward=True,
+                 data_seed=1004, row_seed=2004, head_seed=3004),
+        Workload("fwd_causal_bf16_b1h16n32768d128", 1, 16, 32768, 128, "bf16", causal=True,
+                 data_seed=1005, row_seed=2005, head_seed=3005),
+    ]
+}
+
+
+def normal_tensors(shape, seed: int, count: int, dtype, mults=None):
+    """`count` tensors of i.i.d. N(0,1) values (CPU torch tensors of `dtype`)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for t in range(count):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if mults is not None and mults[t] != 1.0:
+            x *= np.float32(mults[t])
+        out.append(torch.from_numpy(x).to(dtype))
+    return out
+
+
+def make_inputs(w: Workload, with_grad_out: bool | None = None):
+    """Q, K, V (and dO for backward workloads) as contiguous [B,H,N,d] CPU tensors."""
+    with_grad_out = w.backward if with_grad_out is None else with_grad_out
+    shape = (w.B, w.H, w.N, w.d)
+    count = 4 if with_grad_out else 3
+    mults = [w.q_mult, 1.0, 1.0, 1.0][:count]
+    ts = normal_tensors(shape, w.data_seed, count, w.torch_dtype, mults)
+    names = ["q", "k", "v", "do"][:count]
+    return dict(zip(names, ts))
+
+
+def sample_heads(w: Workload, count: int):
+    """`count` distinct (b, h) pairs drawn from the workload's head seed."""
+    rng = np.random.Generator(np.random.PCG64(w.head_seed))
+    flat = rng.choice(w.B * w.H, size=min(count, w.B * w.H), replace=False)
+    return [(int(f) // w.H, int(f) % w.H) for f in flat]
+
+
+def sample_rows(w: Workload, count: int, block_rows=(128,)):
+    """Sorted query rows: the tile-boundary rows plus `count` seeded random rows."""
+    rng = np.random.Generator(np.random.PCG64(w.row_seed))
+    fixed = {0, 1, w.N - 1}
+    for br in block_rows:
+        fixed |= {br - 1, br, min(w.N - 1, 2 * br - 1)}
+    fixed = {r for r in fixed if 0 <= r < w.N}
+    rand = rng.choice(w.N, size=min(count, w.N), replace=False)
+    return np.array(sorted(fixed | {int(r) for r in rand}), dtype=np.int64)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 copy of a CPU tensor (bf16 and fp32 widen exactly)."""
+    return t.detach().to("cpu", torch.float64).numpy()
