@@ -1,1 +1,143 @@
-"""Exact IO-aware attention for MI355X (gfx950): Python binding of libfa.so."""
+"""Exact IO-aware attention for MI355X (gfx950): thin Python binding of libfa.so.
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+include/fa.h. This module only marshals arguments: it checks tensor shapes,
+allocates outputs with torch (device memory and streams are torch's), and
+passes raw pointers and the current HIP stream to the library. There is no
+CPU or PyTorch fallback: if libfa.so is missing, every call raises.
+
+    o, lse = fwd(q, k, v, causal=True)             # q, k, v: [B, H, N, d] bf16 or fp32 on the GPU
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+# (name, restype, argtypes) of every symbol in include/fa.h
+_P, _I, _F, _U64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64, _P]
+_BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64, _P, _SZ, _P]
+SIGNATURES = {
+    "fa_fwd": (_I, _FWD_ARGS),
+    "fa_fwd_f32": (_I, _FWD_ARGS),
+    "fa_bwd": (_I, _BWD_ARGS),
+    "fa_bwd_f32": (_I, _BWD_ARGS),
+    "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "fa_dropout_mask": (_I, [_P, _I, _I, _I, _I, _I, _F, _U64, _P]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().fa_status_string(status).decode()}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa.so with typed entry points; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m exact_io_aware_53_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _shape4(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return tuple(t.shape)
+
+
+def _entry(dtype, stem):
+    if dtype == torch.bfloat16:
+        return getattr(lib(), stem)
+    if dtype == torch.float32:
+        return getattr(lib(), stem + "_f32")
+    raise ValueError("tensors must be bfloat16 or float32")
+
+
+def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out=None, lse=None):
+    """Forward pass: returns (O [B,H,N,d] in the input dtype, LSE [B,H,N] fp32)."""
+    shp = _shape4(q, "q")
+    if _shape4(k, "k") != shp or _shape4(v, "v") != shp or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    B, H, N, d = shp
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _entry(q.dtype, "fa_fwd")(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, scale, int(bool(causal)),
+                                   float(dropout_p), int(seed) & (2**64 - 1), _stream(q.device))
+    _check(st, "fa_fwd")
+    return out, lse
+
+
+def workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass: returns (dQ, dK, dV) in the input dtype."""
+    shp = _shape4(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if _shape4(t, n) != shp or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, do must share shape and dtype")
+    B, H, N, d = shp
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _entry(q.dtype, "fa_bwd")(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), B, H, N, d, scale, int(bool(causal)),
+                                   float(dropout_p), int(seed) & (2**64 - 1),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(q.device))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def dropout_mask(B, H, N, b, h, dropout_p, seed, device="cuda"):
+    """[N, N] uint8 keep mask (1 = kept) of head (b, h), from the device generator."""
+    mask = torch.empty((N, N), dtype=torch.uint8, device=device)
+    st = lib().fa_dropout_mask(mask.data_ptr(), B, H, N, b, h, float(dropout_p),
+                               int(seed) & (2**64 - 1), _stream(mask.device))
+    _check(st, "fa_dropout_mask")
+    return mask
+
+
+__all__ = ["fwd", "bwd", "dropout_mask", "workspace_size", "lib", "FAError", "LIB_PATH",
+           "SIGNATURES"]

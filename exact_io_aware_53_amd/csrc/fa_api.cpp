@@ -1,0 +1,142 @@
+// C ABI of libfa.so: host-side argument validation and dispatch to the gfx950
+// kernels. Every check happens before the first HIP call, so a rejected call
+// touches neither the device nor the stream. See include/fa.h for the contract.
+#include "../../include/fa.h"
+
+#include <math.h>
+
+#include "fa_launch.hpp"
+
+namespace fa {
+
+uint32_t dropout_threshold(float p) {
+    // ceil(p * 2^32) of the float value, exact in double; p < 1 keeps it below 2^32.
+    return (uint32_t)ceil((double)p * 4294967296.0);
+}
+
+}  // namespace fa
+
+namespace {
+
+constexpr long long kMaxElems = 2147483647LL;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int d, float scale, float dropout_p) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;   // also rejects NaN
+    if ((long long)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int B, int H, int N, int d) {
+    const size_t rows = (size_t)B * H * N;
+    return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa::AttnShape shape(int B, int H, int N, int d, float scale, int causal, float p, uint64_t seed) {
+    return fa::AttnShape{B, H, N, d, scale, causal != 0, p, seed};
+}
+
+int fwd_common(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, float dropout_p,
+               uint64_t seed, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale, dropout_p);
+    if (st != FA_OK) return st;
+    fa::FwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, lse};
+    hipStream_t s = (hipStream_t)stream;
+    return map_hip(bf16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+int bwd_common(bool bf16, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int N, int d, float scale, int causal, float dropout_p,
+               uint64_t seed, void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale, dropout_p);
+    if (st != FA_OK) return st;
+    if (ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_INVALID_ARG;
+    const size_t rows = (size_t)B * H * N;
+    float* dq_acc = (float*)workspace;
+    float* dsum = (float*)((char*)workspace + round256(rows * d * sizeof(float)));
+    fa::BwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, dout, lse,
+                  dq, dk, dv, dq_acc, dsum};
+    hipStream_t s = (hipStream_t)stream;
+    return map_hip(bf16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           float dropout_p, uint64_t seed, void* stream) {
+    return fwd_common(true, q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float dropout_p, uint64_t seed, void* stream) {
+    return fwd_common(false, q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes_,
+           void* stream) {
+    return bwd_common(true, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                      dropout_p, seed, workspace, workspace_bytes_, stream);
+}
+
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+               const float* dout, const float* lse, float* dq, float* dk, float* dv,
+               int B, int H, int N, int d, float scale, int causal,
+               float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes_,
+               void* stream) {
+    return bwd_common(false, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                      dropout_p, seed, workspace, workspace_bytes_, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    if ((long long)B * H * N * d > kMaxElems) return 0;
+    return workspace_bytes(B, H, N, d);
+}
+
+int fa_dropout_mask(uint8_t* mask, int B, int H, int N, int b, int h,
+                    float dropout_p, uint64_t seed, void* stream) {
+    if (!mask) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || b < 0 || b >= B || h < 0 || h >= H) return FA_ERR_INVALID_ARG;
+    if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;
+    if ((long long)N * N > kMaxElems) return FA_ERR_INVALID_ARG;
+    return map_hip(fa::launch_dropout_mask(mask, B, H, N, b, h, dropout_p, seed,
+                                           (hipStream_t)stream));
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head size";
+        case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch error";
+        default: return "unknown fa_status";
+    }
+}
+
+}  // extern "C"

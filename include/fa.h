@@ -1,0 +1,136 @@
+/*
+ * fa.h - C ABI of libfa.so: exact, IO-aware scaled dot-product attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * For every batch index b and head h, with Q, K, V the [N, d] matrices of that
+ * head and s = `scale` (the pages fix s = 1/sqrt(d)):
+ *
+ *   S_ij  = s * <Q_i, K_j>                       scaled scores
+ *   A_i   = { j : j <= i } if causal, else all j  (query i never sees later keys)
+ *   LSE_i = log( sum_{j in A_i} exp(S_ij) )       natural log, fp32
+ *   P_ij  = exp(S_ij - LSE_i) for j in A_i, else 0
+ *   O_i   = sum_j P_ij * Z_ij * V_j / (1 - p)     Z = dropout keep mask, all ones if p = 0
+ *
+ * Sources: the scaled score and the online-softmax statistics are those of
+ * "DL0056 FlashAttention" (intvml), section "Mathematical Formulation"; the
+ * result is exact standard attention (same page, answer and point (3); emergent.sh
+ * glossary "Flash Attention", section "Flash Attention vs. Regular Attention").
+ * Causal masking and dropout inside the fused kernel: inferensys glossary
+ * "FlashAttention", paragraph on causal masking and dropout. The forward pass
+ * writes only O and the per-row statistic; the N x N score and probability
+ * matrices never reach device memory (inferensys, paragraph on tiling). The
+ * backward pass recomputes them from the stored statistic instead of storing
+ * them (inferensys, paragraph on recomputation; emergent.sh, "How Flash
+ * Attention Works", step 6) and regenerates the same dropout pattern
+ * (emergent.sh, "Key Components of Flash Attention").
+ *
+ * Dropout mask (the pages name no generator): Z_ij = 1 iff word 0 of
+ * Philox-4x32-10 (Salmon et al., SC'11) at counter (b, h, i, j) under key
+ * (seed & 0xffffffff, seed >> 32) is >= ceil(p * 2^32), p being the float
+ * argument. i and j are absolute row indices inside the head.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, d] arrays, d
+ *   fastest (row-major), element type given by the symbol (bf16 or fp32).
+ *   LSE is a contiguous [B, H, N] fp32 array. Every tensor pointer must be
+ *   16-byte aligned.
+ * - Memory: every pointer is device memory owned by the caller. The library
+ *   never allocates or frees; the backward pass takes its fp32 scratch in
+ *   `workspace`. Inputs must not alias outputs (undefined result, not checked).
+ * - Streams: `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *   asynchronous: a return of FA_OK means the work is enqueued; outputs are
+ *   valid once the stream has been synchronised.
+ * - Errors: arguments are validated on the host before any HIP call.
+ *   FA_ERR_INVALID_ARG  null pointer, B/H/N < 1, dropout_p outside [0, 1),
+ *                       non-finite scale, misaligned pointer, too small a
+ *                       workspace, B*H*N*d above 2^31 - 1.
+ *   FA_ERR_UNSUPPORTED  head size d other than 64 or 128 (the caller keeps its
+ *                       own fallback, as emergent.sh "How to Enable Flash
+ *                       Attention Safely", step 7, advises).
+ *   FA_ERR_HIP          a HIP launch error; the stream state is unspecified.
+ *   No exception or abort crosses the ABI.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,
+    FA_ERR_UNSUPPORTED = 2,
+    FA_ERR_HIP = 3
+} fa_status;
+
+/*
+ * Forward pass, bf16 tensors (fp32 accumulation and softmax).
+ *   q, k, v   in : [B, H, N, d] bf16
+ *   o         out: [B, H, N, d] bf16 (round-to-nearest-even from fp32)
+ *   lse       out: [B, H, N] fp32, natural-log log-sum-exp of the scaled,
+ *                  masked scores, excluding dropout
+ *   scale     score scale s (1/sqrt(d) for standard attention)
+ *   causal    nonzero: query i attends to keys j <= i (top-left aligned)
+ *   dropout_p probability of dropping an attention weight, in [0, 1)
+ *   seed      64-bit dropout seed (ignored when dropout_p == 0)
+ *   stream    hipStream_t to enqueue on
+ * Returns an fa_status. The result is bitwise deterministic run to run.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           float dropout_p, uint64_t seed, void* stream);
+
+/*
+ * Backward pass, bf16 tensors. Given the forward inputs, its outputs O and LSE
+ * (as fa_fwd wrote them, same scale/causal/dropout_p/seed) and the output
+ * gradient dO, writes dQ, dK, dV ([B, H, N, d] bf16).
+ *   workspace        device scratch of at least fa_bwd_workspace_size(B,H,N,d)
+ *                    bytes, 256-byte aligned; contents on entry are ignored.
+ * dQ is accumulated with fp32 atomics, so its last bits may vary run to run.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
+           void* stream);
+
+/* The same two passes for fp32 tensors (fp32 arithmetic throughout). */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float dropout_p, uint64_t seed, void* stream);
+int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+               const float* dout, const float* lse, float* dq, float* dk, float* dv,
+               int B, int H, int N, int d, float scale, int causal,
+               float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * Bytes of device scratch that fa_bwd / fa_bwd_f32 need: an fp32 [B,H,N,d]
+ * dQ accumulator plus the fp32 [B,H,N] row terms D_i = <dO_i, O_i>, each
+ * rounded up to 256 bytes. Returns 0 if an argument is out of range.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Test aid: writes the dropout keep mask Z of head (b, h) as an [N, N] array
+ * of bytes (1 = kept, 0 = dropped) into device memory `mask`, using the same
+ * device generator as the attention kernels. Causal masking is not applied.
+ */
+int fa_dropout_mask(uint8_t* mask, int B, int H, int N, int b, int h,
+                    float dropout_p, uint64_t seed, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

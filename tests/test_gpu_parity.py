@@ -1,0 +1,286 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances: fp32 tensors max |err| <= 1e-5 (O, LSE and gradients); bf16
+tensors O <= 1e-2, LSE <= 1e-3, gradients max|g - g_ref| / max|g_ref| <= 2e-2;
+dropout masks bit-exact. Small shapes are checked on every row of every
+head; the full-size workloads on seeded heads and rows (full rows always).
+
+Two readings of those bounds, both forced by the output dtype:
+* O is stored in bf16. Where |O_ref| >= 4 (rows that mix only a few keys,
+  e.g. causal row 0 scaled by 1/(1-p)), half a bf16 ulp alone exceeds 1e-2,
+  so no bf16 result could meet it. There the bound per element is
+  half an ulp of O_ref plus 2^-9 |O_ref| (the rounding of P to bf16); below
+  |O_ref| = 4 that expression is under 1e-2 and the plain bound applies.
+* A gradient whose reference is identically zero (one key, or a dropped
+  single key) has no "max"; it is measured relative to the largest reference
+  gradient of the same head, or absolutely if all three are zero.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_53_amd as fa
+import oracle
+from exact_io_aware_53_amd.inputs import (WORKLOADS, make_inputs, normal_tensors, sample_heads,
+                                          sample_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": dict(o=1e-2, lse=1e-3, grad=2e-2), "f32": dict(o=1e-5, lse=1e-5, grad=1e-5)}
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+SEED = 0x0123456789ABCDEF
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()   # fails loudly when the library is missing
+
+
+def upload(ts):
+    return [t.to("cuda") for t in ts]
+
+
+def check_forward_heads(q, k, v, o, lse, causal, p, seed, tol, heads, rows=None, tag=""):
+    """Compare O and LSE of the given heads (all rows, or `rows`) with the oracle."""
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d)
+    o_c, lse_c = o.float().cpu(), lse.cpu()
+    worst_o = worst_l = 0.0
+    for (b, h) in heads:
+        ro, rl = oracle.forward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale,
+                                causal, p, seed, b, h, rows=rows)
+        go = o_c[b, h].double().numpy()
+        gl = lse_c[b, h].double().numpy()
+        if rows is not None:
+            go, gl = go[rows], gl[rows]
+        excess = np.abs(go - ro) / o_bound(ro, tol["o"], o.dtype)
+        eo, el = excess.max() * tol["o"], np.abs(gl - rl).max()
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    assert worst_o <= tol["o"], f"{tag} O max err (scaled to the 1e-2 bound) {worst_o:.3e}"
+    assert worst_l <= tol["lse"], f"{tag} LSE max err {worst_l:.3e}"
+    return worst_o, worst_l
+
+
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 numbers at |x| (8 significand bits)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+def o_bound(ref, tol, dtype):
+    """Per-element O bound: tol, widened only where bf16 storage alone exceeds it."""
+    if dtype != torch.bfloat16:
+        return np.full(ref.shape, tol)
+    return np.maximum(tol, bf16_half_ulp(ref) + np.abs(ref) * 2.0 ** -9)
+
+
+def rel_to_max(g, ref, fallback=None):
+    denom = np.abs(ref).max()
+    if denom == 0.0:
+        denom = fallback if fallback else 1.0
+    return float(np.abs(g - ref).max() / denom)
+
+
+def abs_err(g, ref):
+    return float(np.abs(g - ref).max())
+
+
+SMALL = [(1, 2, 1, 64), (1, 2, 17, 64), (2, 1, 127, 128), (1, 1, 128, 64), (1, 2, 129, 128),
+         (1, 1, 1000, 64), (2, 2, 300, 128), (1, 1, 64, 128), (3, 1, 257, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.1])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_forward_small(shape, causal, p, dtype):
+    B, H, N, d = shape
+    seed_data = 17 + N + 7 * d + B
+    q, k, v = normal_tensors(shape, seed_data, 3, DTYPES[dtype])
+    gq, gk, gv = upload((q, k, v))
+    o, lse = fa.fwd(gq, gk, gv, causal=causal, dropout_p=p, seed=SEED)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL[dtype], heads, tag=str(shape))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.1])
+@pytest.mark.parametrize("shape", [(1, 2, 17, 64), (2, 1, 129, 128), (1, 1, 256, 64),
+                                   (1, 2, 300, 128), (1, 1, 1, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_small(shape, causal, p, dtype):
+    B, H, N, d = shape
+    q, k, v, do = normal_tensors(shape, 911 + N + d, 4, DTYPES[dtype])
+    gq, gk, gv, gdo = upload((q, k, v, do))
+    o, lse = fa.fwd(gq, gk, gv, causal=causal, dropout_p=p, seed=SEED)
+    dq, dk, dv = fa.bwd(gq, gk, gv, o, lse, gdo, causal=causal, dropout_p=p, seed=SEED)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            rq, rk, rv, _ = oracle.backward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
+                                            to_f64(do[b, h]), scale, causal, p, SEED, b, h)
+            head_max = max(np.abs(r).max() for r in (rq, rk, rv))
+            for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+                got = g[b, h].double().cpu().numpy()
+                worst = max(worst, abs_err(got, r) if dtype == "f32" else rel_to_max(got, r, head_max))
+    assert worst <= TOL[dtype]["grad"], f"grad err {worst:.3e}"
+
+
+# ------------------------------------------------------------ full workloads
+def run_workload_forward(w):
+    t = make_inputs(w)
+    gq, gk, gv = upload((t["q"], t["k"], t["v"]))
+    o, lse = fa.fwd(gq, gk, gv, causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed)
+    torch.cuda.synchronize()
+    return t, (gq, gk, gv), o, lse
+
+
+def test_workload_f32_b1h1n128d64():
+    w = WORKLOADS["fwd_f32_b1h1n128d64"]
+    t, _, o, lse = run_workload_forward(w)
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, w.causal, 0.0, 0, TOL["f32"], [(0, 0)])
+
+
+def test_workload_causal_b4h16n2048d64():
+    w = WORKLOADS["fwd_causal_bf16_b4h16n2048d64"]
+    t, _, o, lse = run_workload_forward(w)
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
+                        sample_heads(w, 2))
+
+
+def test_workload_causal_q4_b2h32n8192d128():
+    w = WORKLOADS["fwd_causal_q4_bf16_b2h32n8192d128"]
+    t, _, o, lse = run_workload_forward(w)
+    rows = sample_rows(w, 256, block_rows=(64, 128, 256))
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
+                        sample_heads(w, 2), rows=rows)
+
+
+def test_workload_causal_b1h16n32768d128():
+    w = WORKLOADS["fwd_causal_bf16_b1h16n32768d128"]
+    t, _, o, lse = run_workload_forward(w)
+    rows = sample_rows(w, 64, block_rows=(64, 128, 256))
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
+                        sample_heads(w, 2), rows=rows)
+
+
+def test_workload_dropout_fwd_bwd_b2h16n4096d64():
+    w = WORKLOADS["fwdbwd_causal_dropout_bf16_b2h16n4096d64"]
+    t = make_inputs(w)
+    gq, gk, gv, gdo = upload((t["q"], t["k"], t["v"], t["do"]))
+    o, lse = fa.fwd(gq, gk, gv, causal=True, dropout_p=w.dropout_p, seed=w.dropout_seed)
+    dq, dk, dv = fa.bwd(gq, gk, gv, o, lse, gdo, causal=True, dropout_p=w.dropout_p,
+                        seed=w.dropout_seed)
+    torch.cuda.synchronize()
+    (b, h), = sample_heads(w, 1)
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, w.dropout_p, w.dropout_seed,
+                        TOL["bf16"], [(b, h)])
+    rq, rk, rv, _ = oracle.backward(to_f64(t["q"][b, h]), to_f64(t["k"][b, h]),
+                                    to_f64(t["v"][b, h]), to_f64(t["do"][b, h]), w.scale, True,
+                                    w.dropout_p, w.dropout_seed, b, h)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        e = rel_to_max(g[b, h].double().cpu().numpy(), r)
+        assert e <= TOL["bf16"]["grad"], f"{name} rel-to-max err {e:.3e}"
+
+
+# --------------------------------------------------------- dropout mask probes
+def test_dropout_mask_bit_exact_one_head():
+    w = WORKLOADS["fwdbwd_causal_dropout_bf16_b2h16n4096d64"]
+    (b, h), = sample_heads(w, 1)
+    m = fa.dropout_mask(w.B, w.H, w.N, b, h, w.dropout_p, w.dropout_seed).cpu().numpy()
+    for i0 in range(0, w.N, 1024):
+        rows = np.arange(i0, i0 + 1024)
+        ref = oracle.keep_mask(b, h, rows, np.arange(w.N), w.dropout_p, w.dropout_seed)
+        assert np.array_equal(m[rows].astype(bool), ref)
+
+
+def test_dropout_mask_through_forward_kernel():
+    """V = one-hot columns makes O[i, c] = P_{i j_c} Z_{i j_c} / (1-p): the forward kernel's
+    mask for 64 keys per launch, compared bit-exactly with the oracle's."""
+    B, H, N, d, p = 1, 2, 512, 64, 0.1
+    q, k = normal_tensors((B, H, N, d), 5150, 2, torch.bfloat16)
+    gq, gk = upload((q, k))
+    for j0 in (0, 200, 448):
+        v = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+        cols = np.arange(j0, j0 + d)
+        v[:, :, torch.as_tensor(cols), torch.arange(d)] = 1.0
+        o, _ = fa.fwd(gq, gk, v.cuda(), causal=False, dropout_p=p, seed=SEED)
+        got = (o.float().cpu().numpy() != 0)
+        for h in range(H):
+            ref = oracle.keep_mask(0, h, np.arange(N), cols, p, SEED)
+            assert np.array_equal(got[0, h], ref), (j0, h)
+
+
+def test_dropout_mask_through_backward_kernel():
+    """dO rows i_c = e_c give dV_j[c] = P_{i_c j} Z_{i_c j} / (1-p): 64 mask rows per launch."""
+    B, H, N, d, p = 1, 1, 384, 64, 0.1
+    q, k, v = normal_tensors((B, H, N, d), 6160, 3, torch.bfloat16)
+    gq, gk, gv = upload((q, k, v))
+    o, lse = fa.fwd(gq, gk, gv, causal=False, dropout_p=p, seed=SEED)
+    for i0 in (0, 130, 320):
+        do = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+        rows = np.arange(i0, i0 + d)
+        do[:, :, torch.as_tensor(rows), torch.arange(d)] = 1.0
+        _, _, dv = fa.bwd(gq, gk, gv, o, lse, do.cuda(), causal=False, dropout_p=p, seed=SEED)
+        got = (dv.float().cpu().numpy()[0, 0] != 0).T        # [c, j]
+        ref = oracle.keep_mask(0, 0, rows, np.arange(N), p, SEED)
+        assert np.array_equal(got, ref), i0
+
+
+# ------------------------------------------------------------ other properties
+def test_forward_is_deterministic():
+    shape = (2, 4, 1000, 128)
+    q, k, v = upload(normal_tensors(shape, 7007, 3, torch.bfloat16))
+    outs = [fa.fwd(q, k, v, causal=True, dropout_p=0.1, seed=SEED) for _ in range(3)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_outputs_stay_in_bounds(dtype):
+    """Canary words around every output buffer are untouched."""
+    B, H, N, d = 1, 3, 333, 64
+    dt = DTYPES[dtype]
+    q, k, v, do = upload(normal_tensors((B, H, N, d), 8118, 4, dt))
+    n = B * H * N * d
+    pad = 4096
+
+    def guarded(count, tdt):
+        buf = torch.full((count + 2 * pad,), 7.0, dtype=tdt, device="cuda")
+        return buf, buf[pad:pad + count]
+
+    ob, o = guarded(n, dt)
+    lb, lse = guarded(B * H * N, torch.float32)
+    fa.fwd(q, k, v, causal=True, dropout_p=0.1, seed=SEED, out=o.view(B, H, N, d),
+           lse=lse.view(B, H, N))
+    grads = [guarded(n, dt) for _ in range(3)]
+    fa.bwd(q, k, v, o.view(B, H, N, d), lse.view(B, H, N), do, causal=True, dropout_p=0.1,
+           seed=SEED, dq=grads[0][1].view(B, H, N, d), dk=grads[1][1].view(B, H, N, d),
+           dv=grads[2][1].view(B, H, N, d))
+    torch.cuda.synchronize()
+    for buf, _ in [(ob, o), (lb, lse)] + grads:
+        assert torch.all(buf[:pad] == 7.0) and torch.all(buf[-pad:] == 7.0)
+
+
+def test_uniform_scores_and_causal_row0_on_gpu():
+    """Closed forms through the kernels: Q = 0 gives O_i = mean of visible V rows and
+    LSE_i = ln(i+1) (causal); causal row 0 returns V_0 exactly."""
+    B, H, N, d = 1, 1, 300, 128
+    k, v = normal_tensors((B, H, N, d), 9119, 2, torch.bfloat16)
+    q = torch.zeros_like(k)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=True)
+    vv = to_f64(v[0, 0])
+    mean = np.cumsum(vv, axis=0) / np.arange(1, N + 1)[:, None]
+    assert np.abs(o[0, 0].double().cpu().numpy() - mean).max() <= 1e-2
+    assert np.abs(lse[0, 0].double().cpu().numpy() - np.log(np.arange(1, N + 1))).max() <= 1e-3
+    q2 = normal_tensors((B, H, N, d), 9120, 1, torch.bfloat16)[0]
+    o2, _ = fa.fwd(*upload((q2, k, v)), causal=True)
+    assert torch.equal(o2[0, 0, 0].cpu(), v[0, 0, 0])
