@@ -1,0 +1,215 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the path over one batch of synthetic inputs already
+resident in HBM. The default workload is the causal bf16 softmax-stress
+forward (B=2, H=32, N=8192, d=128, Q scaled by 4). The same JSON line also
+carries the forward+backward measurement on the dropout workload
+(B=2, H=16, N=4096, d=64, p=0.1), the roofline of the dominant kernel and the
+CPU oracle's throughput on a bounded sample.
+
+FLOPs are counted as 4*B*H*N^2*d for the forward, halved when causal, and
+2.5x that for the backward.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd; fwd+bwd) and % of MI355X bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "fwd_causal_q4_bf16_b2h32n8192d128"
+FWD_BWD_WORKLOAD = "fwdbwd_causal_dropout_bf16_b2h16n4096d64"
+FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp"]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    no summary exists for this workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_bf16_{workload_name}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, flags=re.M))
+    if fields.get("source_hash") != source_hash(FWD_SOURCES):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn warmup times, then `steps` timed times; returns (wall ms/step, per-launch event ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """The CPU oracle (unchanged) on whole heads of the workload until ~budget_s of work."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from exact_io_aware_53_amd.inputs import to_f64
+
+    threads = max(int(info.get("num_threads", 1)) for info in threadpoolctl.threadpool_info()) \
+        if threadpoolctl.threadpool_info() else 1
+    heads_done, rows_done, flops = 0, 0, 0.0
+    t0 = time.perf_counter()
+    chunk = 1024
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        q, k, v = (to_f64(inputs[n][b, h]) for n in ("q", "k", "v"))
+        for r0 in range(0, w.N, chunk):
+            rows = np.arange(r0, min(w.N, r0 + chunk))
+            oracle.forward(q, k, v, w.scale, w.causal, w.dropout_p, w.dropout_seed, b, h, rows=rows)
+            rows_done += len(rows)
+        heads_done += 1
+        flops += w.fwd_flops() / (w.B * w.H)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads_done} of {w.B * w.H} heads ({rows_done} query rows, all keys) of "
+                      f"{w.name}, fp64 NumPy, {dt:.1f} s; FLOPs counted as for the GPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fwd-bwd", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(every workload fits one MI355X). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_53_amd as fa
+    from exact_io_aware_53_amd.inputs import WORKLOADS, make_inputs
+
+    fa.lib()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    host = make_inputs(w, with_grad_out=False)
+    q, k, v = (host[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    def fwd_step():
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, dropout_p=w.dropout_p,
+               seed=w.dropout_seed, out=o, lse=lse)
+
+    wall_ms, ev_ms = time_launches(fwd_step, args.steps, args.warmup, stream)
+    peak_extra = torch.cuda.max_memory_allocated(dev) - mem0
+    kern_ms = sum(ev_ms) / len(ev_ms)
+    flops = w.fwd_flops()
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = counter_traffic(w.name)
+    io_bytes = (4 * w.B * w.H * w.N * w.d * q.element_size()) + 4 * w.B * w.H * w.N
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) Q, K, V (Q x4 where the workload says so)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "dropout_p": w.dropout_p, "q_mult": w.q_mult,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "fwd_bf16_kernel",
+                     "kernel_ms": round(kern_ms, 4), "ideal_io_bytes": io_bytes},
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "peak_extra_device_bytes": int(peak_extra),
+    }
+
+    if not args.no_fwd_bwd:
+        w2 = WORKLOADS[FWD_BWD_WORKLOAD]
+        h2 = make_inputs(w2)
+        q2, k2, v2, do2 = (h2[n].to(dev) for n in ("q", "k", "v", "do"))
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device=dev)
+        dq2, dk2, dv2 = torch.empty_like(q2), torch.empty_like(k2), torch.empty_like(v2)
+        ws = torch.empty(fa.workspace_size(w2.B, w2.H, w2.N, w2.d), dtype=torch.uint8, device=dev)
+
+        def f2():
+            fa.fwd(q2, k2, v2, scale=w2.scale, causal=True, dropout_p=w2.dropout_p,
+                   seed=w2.dropout_seed, out=o2, lse=l2)
+
+        def b2():
+            fa.bwd(q2, k2, v2, o2, l2, do2, scale=w2.scale, causal=True, dropout_p=w2.dropout_p,
+                   seed=w2.dropout_seed, dq=dq2, dk=dk2, dv=dv2, workspace=ws)
+
+        f2()
+        tf, _ = time_launches(f2, args.steps, args.warmup, stream)
+        tb, _ = time_launches(b2, args.steps, args.warmup, stream)
+        line["fwd_bwd"] = {
+            "workload": w2.name, "ms_fwd": round(tf, 4), "ms_bwd": round(tb, 4),
+            "tflops_fwd": round(w2.fwd_flops() / (tf * 1e-3) / 1e12, 3),
+            "tflops_bwd": round(w2.bwd_flops() / (tb * 1e-3) / 1e12, 3),
+            "tflops_fwd_bwd": round((w2.fwd_flops() + w2.bwd_flops()) / ((tf + tb) * 1e-3) / 1e12, 3),
+        }
+        del q2, k2, v2, do2, o2, l2, dq2, dk2, dv2, ws
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

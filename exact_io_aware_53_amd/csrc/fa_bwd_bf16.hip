@@ -1,11 +1,403 @@
-// Backward attention for bf16 tensors.
+// Backward attention for bf16 tensors on gfx950 matrix cores.
+//
+// Recomputation instead of storage (inferensys glossary "FlashAttention",
+// paragraph on recomputation; emergent.sh glossary "Flash Attention", "How
+// Flash Attention Works", step 6): the score and probability tiles are rebuilt
+// from Q, K and the stored row log-sum-exp, P = exp(S - LSE), tile by tile,
+// and the dropout pattern is regenerated from the same Philox counters
+// (emergent.sh, "Key Components of Flash Attention"). The gradients are those
+// of exact attention, fused into one kernel per key block (DL0056
+// FlashAttention, point (3)):
+//
+//   D_i  = <dO_i, O_i>                   (pre-pass, fp32)
+//   dV_j += sum_i P_ij Z'_ij dO_i         Z' = Z / (1 - p)
+//   dP_ij = <dO_i, V_j> Z'_ij
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dK_j += s sum_i dS_ij Q_i,   dQ_i += s sum_j dS_ij K_j   (fp32 atomics)
+//
+// gfx950 mapping
+// --------------
+// * A workgroup of 4 waves owns 128 keys (32 per wave). K and V rows of the
+//   wave's keys stay in registers as matrix-core operands; dK and dV
+//   accumulate in registers over every query tile, transposed (d x keys).
+// * Query tiles of 64 rows (Q, dO, LSE, D) stream HBM -> LDS through
+//   buffer_load ... lds; the next tile is fetched while the current one's dQ
+//   products run.
+// * S = Q K^T and dP = dO V^T leave a lane holding one key and 16 query rows,
+//   which is exactly the B-operand layout that dV^T = dO^T (P Z') and
+//   dK^T = Q^T dS need; dO^T and Q^T come from LDS through ds_read_b64_tr_b16.
+// * dS goes to LDS (transposed, bf16) once per tile; the four waves then form
+//   dQ_tile = dS K for all 128 keys and add it to an fp32 accumulator in HBM
+//   with global atomics. A last pass converts that accumulator to bf16.
+// * LDS rows are XOR-swizzled in 16-byte chunks with one pattern that keeps
+//   both access shapes conflict-free: 8 rows x 16 bytes (row operands) and
+//   4 rows x 32 bytes (transposed reads).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
+namespace {
 
-hipError_t launch_bwd_bf16_simple(const BwdArgs& a, hipStream_t st);
+constexpr int kBKV = 128;     // keys per workgroup
+constexpr int kNW = 4;        // waves per workgroup (32 keys each)
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) { return launch_bwd_bf16_simple(a, st); }
+struct BwdParamsB {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const __bf16* dout;
+    const float* lse;
+    const float* dsum;
+    float* dq_acc;
+    __bf16* dk;
+    __bf16* dv;
+    int H, N, nkb, heads;
+    float scale, sl2, inv_keep;
+    uint32_t thr;
+    PhiloxKey key;
+};
+
+// Chunk swizzle: a permutation of 0..7 over any 8 aligned rows, and distinct
+// chunk pairs over any 4 aligned rows.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+__device__ __forceinline__ int lds_off(int row, int col, int row_bytes) {
+    return row * row_bytes + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+}
+
+// Operand whose matrix-core contraction index runs along LDS columns: lane
+// holds row r0 + lane%32, columns c0 + 8*(lane/32) .. +7.
+__device__ __forceinline__ bf16x8 row_operand(const FA_LDS char* base, int row_bytes, int r0, int c0,
+                                              int lane) {
+    const int row = r0 + (lane & 31);
+    const int col = c0 + 8 * (lane >> 5);
+    return *(const FA_LDS bf16x8*)(base + lds_off(row, col, row_bytes));
+}
+
+// Operand whose contraction index runs along LDS rows: lane holds column
+// c0 + lane%32 and rows r0 + 4*(lane/32) + {0..3}, r0 + 8 + 4*(lane/32) + {0..3}
+// (the order in which a 32x32 accumulator holds its rows).
+__device__ __forceinline__ bf16x8 tr_operand(const FA_LDS char* base, int row_bytes, int r0, int c0,
+                                             int lane) {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int col = c0 + 16 * (grp & 1) + 4 * (sl & 3);
+    bf16x8 a;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int row = r0 + 8 * half + 4 * (grp >> 1) + (sl >> 2);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS s16x4*)(base + lds_off(row, col, row_bytes)));
+        const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
+    }
+    return a;
+}
+
+template <int D, int BQ, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
+    constexpr int CH = D / 8;
+    constexpr int QB = BQ / 32;        // 32-row query blocks per tile
+    constexpr int DB = D / 32;
+    constexpr int NCD = D / 16;        // 16-wide d chunks (contraction of S and dP)
+    constexpr int TILE = BQ * D * 2;
+    constexpr int QLOADS = BQ * CH / (64 * kNW);
+    constexpr int KLOADS = kBKV * CH / (64 * kNW);
+    static_assert(QLOADS * 64 * kNW == BQ * CH, "query tile must split over the waves");
+    static_assert(BQ == 64, "dS^T rows need 8 chunks for the swizzle");
+
+    __shared__ __attribute__((aligned(1024))) char q_s[TILE];
+    __shared__ __attribute__((aligned(1024))) char do_s[TILE];
+    __shared__ __attribute__((aligned(1024))) char k_s[kBKV * D * 2];
+    __shared__ __attribute__((aligned(1024))) char dst_s[kBKV * BQ * 2];
+    __shared__ float lse_s[BQ];
+    __shared__ float dsum_s[BQ];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    FA_LDS char* const qL = (FA_LDS char*)q_s;
+    FA_LDS char* const doL = (FA_LDS char*)do_s;
+    FA_LDS char* const kL = (FA_LDS char*)k_s;
+    FA_LDS char* const dsL = (FA_LDS char*)dst_s;
+
+    int bh, kb;
+    const int bid = blockIdx.x;
+    if ((p.heads & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        bh = (slot / p.nkb) * 8 + xcd;
+        kb = slot % p.nkb;
+    } else {
+        bh = bid % p.heads;
+        kb = bid / p.heads;
+    }
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int N = p.N;
+    const size_t head = (size_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const auto rs_q = make_rsrc(p.q + head, head_bytes);
+    const auto rs_k = make_rsrc(p.k + head, head_bytes);
+    const auto rs_v = make_rsrc(p.v + head, head_bytes);
+    const auto rs_do = make_rsrc(p.dout + head, head_bytes);
+    const auto rs_lse = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+    const auto rs_ds = make_rsrc(p.dsum + (size_t)bh * N, (uint32_t)N * 4);
+
+    const int j0 = kb * kBKV;
+    const int kw = j0 + wave * 32;     // first key of this wave
+    const int my_key = kw + l32;
+
+    // K and V rows of this wave's keys as B operands (d chunk c: d = 16c + 8hi .. +7)
+    bf16x8 kt[NCD], vt[NCD];
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) {
+        const uint32_t off = (uint32_t)(my_key * D + 16 * c + 8 * hi) * 2;
+        kt[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_k, off));
+        vt[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_v, off));
+    }
+    // All 128 keys of the block into LDS for the dQ products.
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+        const int blk = i * kNW + wave, pos = blk * 64 + lane;
+        const int row = pos / CH, sw = pos % CH;
+        buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
+                        (uint32_t)((j0 + row) * D + ((sw ^ swz(row)) << 3)) * 2);
+    }
+
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dva[i][r] = dka[i][r] = 0.0f;
+
+    auto issue_tile = [&](int i0) {
+#pragma unroll
+        for (int i = 0; i < QLOADS; ++i) {
+            const int blk = i * kNW + wave, pos = blk * 64 + lane;
+            const int row = pos / CH, sw = pos % CH;
+            const uint32_t off = (uint32_t)((i0 + row) * D + ((sw ^ swz(row)) << 3)) * 2;
+            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + blk * 1024), off);
+            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + blk * 1024), off);
+        }
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)lse_s, 4,
+                                                     (uint32_t)(i0 + lane) * 4, 0, 0, 0);
+        if (wave == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)dsum_s, 4,
+                                                     (uint32_t)(i0 + lane) * 4, 0, 0, 0);
+    };
+
+    const int i_begin = CAUSAL ? j0 : 0;
+    if (i_begin < N) issue_tile(i_begin);
+
+    for (int i0 = i_begin; i0 < N; i0 += BQ) {
+        wait_vmem();
+        __syncthreads();
+
+        const bool skip = CAUSAL && kw > i0 + BQ - 1;    // every query of the tile precedes our keys
+        if (skip) {
+            // this wave's rows of dS^T are zero for this tile
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(FA_LDS u32x2*)(dsL + lds_off(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi, BQ * 2)) =
+                        u32x2{0u, 0u};
+        } else {
+            f32x16 s[QB], dp[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCD; ++c) {
+                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        row_operand(qL, D * 2, qb * 32, 16 * c, lane), kt[c], s[qb], 0, 0, 0);
+                    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        row_operand(doL, D * 2, qb * 32, 16 * c, lane), vt[c], dp[qb], 0, 0, 0);
+                }
+            }
+            const bool need_mask = (CAUSAL && i0 < kw + 31) || (kw + 32 > N) || (i0 + BQ > N);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qrow = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const int qi = i0 + qrow;
+                    float pr = fast_exp2(fmaf(s[qb][r], p.sl2, -lse_s[qrow] * kLog2e));
+                    if (need_mask) {
+                        const bool live = qi < N && my_key < N && (!CAUSAL || my_key <= qi);
+                        if (!live) pr = 0.0f;
+                    }
+                    float z = 1.0f;
+                    if (DROPOUT) {
+                        const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)qi,
+                                                        (uint32_t)my_key, p.key);
+                        z = w >= p.thr ? p.inv_keep : 0.0f;
+                    }
+                    const float ds = pr * fmaf(dp[qb][r], z, -dsum_s[qrow]);
+                    s[qb][r] = pr * z;      // P Z' for dV
+                    dp[qb][r] = ds;         // dS
+                }
+            // dV^T += dO^T (P Z'),  dK^T += Q^T dS  (contraction over the tile's query rows)
+#pragma unroll
+            for (int qc = 0; qc < BQ / 16; ++qc) {
+                bf16x8 bp, bs;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    bp[i] = (__bf16)s[qc >> 1][8 * (qc & 1) + i];
+                    bs[i] = (__bf16)dp[qc >> 1][8 * (qc & 1) + i];
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_operand(doL, D * 2, 16 * qc, 32 * db, lane), bp, dva[db], 0, 0, 0);
+                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_operand(qL, D * 2, 16 * qc, 32 * db, lane), bs, dka[db], 0, 0, 0);
+                }
+            }
+            // dS^T (bf16) to LDS: row = key within the block, columns = query rows
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(dp[qb][4 * g + 0], dp[qb][4 * g + 1]);
+                    w[1] = pack_bf16x2(dp[qb][4 * g + 2], dp[qb][4 * g + 3]);
+                    *(FA_LDS u32x2*)(dsL + lds_off(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi, BQ * 2)) = w;
+                }
+        }
+        __syncthreads();
+        if (i0 + BQ < N) issue_tile(i0 + BQ);     // Q/dO/LSE/D are not read again this tile
+
+        // dQ_tile = dS K over the block's 128 keys, 32x32 blocks dealt to the waves
+#pragma unroll
+        for (int blk = wave; blk < QB * DB; blk += kNW) {
+            const int qb = blk / DB, db = blk % DB;
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < kBKV / 16; ++kc)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    tr_operand(dsL, BQ * 2, 16 * kc, 32 * qb, lane),
+                    tr_operand(kL, D * 2, 16 * kc, 32 * db, lane), acc, 0, 0, 0);
+            float* dst = p.dq_acc + head + 32 * db + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (qi < N) atomicAdd(dst + (size_t)qi * D, acc[r] * p.scale);
+            }
+        }
+    }
+
+    // dK = s dK^T, dV = dV^T, transposed on the way out (lane = key, registers = d)
+    if (my_key < N) {
+        __bf16* dkr = p.dk + head + (size_t)my_key * D;
+        __bf16* dvr = p.dv + head + (size_t)my_key * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 wk, wv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wk[i] = (__bf16)(dka[db][4 * g + i] * p.scale);
+                    wv[i] = (__bf16)dva[db][4 * g + i];
+                }
+                *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hi) = wk;
+                *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+    }
+}
+
+// D_i = <dO_i, O_i> in fp32 and a zeroed dQ accumulator; 8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __bf16* dout,
+                                                      float* dsum, float* dq_acc, int rows) {
+    constexpr int PER = D / 8;     // elements per lane
+    const int row = blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    float acc = 0.0f;
+    if (row < rows) {
+        const size_t base = (size_t)row * D + part * PER;
+#pragma unroll
+        for (int c = 0; c < PER; c += 8) {
+            const bf16x8 a = *(const bf16x8*)(o + base + c);
+            const bf16x8 g = *(const bf16x8*)(dout + base + c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)g[i], acc);
+            *(f32x4*)(dq_acc + base + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *(f32x4*)(dq_acc + base + c + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (row < rows && part == 0) dsum[row] = acc;
+}
+
+// dQ = bf16(dQ accumulator), 8 elements per thread.
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, __bf16* dq, size_t n8) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const f32x4 a = *(const f32x4*)(acc + 8 * i);
+    const f32x4 b = *(const f32x4*)(acc + 8 * i + 4);
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        r[t] = (__bf16)a[t];
+        r[4 + t] = (__bf16)b[t];
+    }
+    *(bf16x8*)(dq + 8 * i) = r;
+}
+
+template <int D, bool CAUSAL, bool DROPOUT>
+hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
+    BwdParamsB p{};
+    p.q = (const __bf16*)a.q;
+    p.k = (const __bf16*)a.k;
+    p.v = (const __bf16*)a.v;
+    p.dout = (const __bf16*)a.dout;
+    p.lse = a.lse;
+    p.dsum = a.dsum;
+    p.dq_acc = a.dq_accum;
+    p.dk = (__bf16*)a.dk;
+    p.dv = (__bf16*)a.dv;
+    p.H = a.s.H;
+    p.N = a.s.N;
+    p.nkb = (a.s.N + kBKV - 1) / kBKV;
+    p.heads = a.s.B * a.s.H;
+    p.scale = a.s.scale;
+    p.sl2 = a.s.scale * kLog2e;
+    p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
+    p.thr = dropout_threshold(a.s.dropout_p);
+    p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 64, CAUSAL, DROPOUT>), dim3(p.heads * p.nkb),
+                       dim3(kNW * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
+    const int rows = a.s.B * a.s.H * a.s.N;
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 31) / 32), dim3(256), 0, st,
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.dsum, a.dq_accum, rows);
+    const bool drop = dropout_threshold(a.s.dropout_p) != 0;
+    hipError_t e;
+    if (a.s.causal)
+        e = drop ? launch_main<D, true, true>(a, st) : launch_main<D, true, false>(a, st);
+    else
+        e = drop ? launch_main<D, false, true>(a, st) : launch_main<D, false, false>(a, st);
+    if (e != hipSuccess) return e;
+    const size_t n8 = (size_t)rows * D / 8;
+    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)a.dq_accum, (__bf16*)a.dq, n8);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
+    return a.s.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
 
 }  // namespace fa
