@@ -19,9 +19,12 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU forms are kept out of the generated code.
+# Packed-fp32 VALU forms are kept out of the generated code. Matrix-core
+# results are kept in architectural VGPRs, so the softmax can work on them
+# without copies out of the accumulation registers.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wno-unused-command-line-argument"]
 
 
@@ -37,30 +40,31 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, defines=(), build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-x", "hip", *COMMON, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), lib_path: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source (optionally with extra -D defines) and link `lib_path`."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, defines, build_dir), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib_path} from {len(srcs)} sources")
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -29,9 +29,8 @@
 // * dS goes to LDS (transposed, bf16) once per tile; the four waves then form
 //   dQ_tile = dS K for all 128 keys and add it to an fp32 accumulator in HBM
 //   with global atomics. A last pass converts that accumulator to bf16.
-// * LDS rows are XOR-swizzled in 16-byte chunks with one pattern that keeps
-//   both access shapes conflict-free: 8 rows x 16 bytes (row operands) and
-//   4 rows x 32 bytes (transposed reads).
+// * LDS rows are XOR-swizzled in 16-byte chunks (chunk_swizzle) so that both
+//   access shapes, row operands and transposed reads, are conflict-free.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -57,28 +56,20 @@ struct BwdParamsB {
     PhiloxKey key;
 };
 
-// Chunk swizzle: a permutation of 0..7 over any 8 aligned rows, and distinct
-// chunk pairs over any 4 aligned rows.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-__device__ __forceinline__ int lds_off(int row, int col, int row_bytes) {
-    return row * row_bytes + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
-}
-
 // Operand whose matrix-core contraction index runs along LDS columns: lane
 // holds row r0 + lane%32, columns c0 + 8*(lane/32) .. +7.
-__device__ __forceinline__ bf16x8 row_operand(const FA_LDS char* base, int row_bytes, int r0, int c0,
-                                              int lane) {
+template <int CPR>
+__device__ __forceinline__ bf16x8 row_operand(const FA_LDS char* base, int r0, int c0, int lane) {
     const int row = r0 + (lane & 31);
     const int col = c0 + 8 * (lane >> 5);
-    return *(const FA_LDS bf16x8*)(base + lds_off(row, col, row_bytes));
+    return *(const FA_LDS bf16x8*)(base + tile_offset<CPR>(row, col));
 }
 
 // Operand whose contraction index runs along LDS rows: lane holds column
 // c0 + lane%32 and rows r0 + 4*(lane/32) + {0..3}, r0 + 8 + 4*(lane/32) + {0..3}
 // (the order in which a 32x32 accumulator holds its rows).
-__device__ __forceinline__ bf16x8 tr_operand(const FA_LDS char* base, int row_bytes, int r0, int c0,
-                                             int lane) {
+template <int CPR>
+__device__ __forceinline__ bf16x8 tr_operand(const FA_LDS char* base, int r0, int c0, int lane) {
     const int grp = lane >> 4, sl = lane & 15;
     const int col = c0 + 16 * (grp & 1) + 4 * (sl & 3);
     bf16x8 a;
@@ -86,7 +77,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const FA_LDS char* base, int row_by
     for (int half = 0; half < 2; ++half) {
         const int row = r0 + 8 * half + 4 * (grp >> 1) + (sl >> 2);
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS s16x4*)(base + lds_off(row, col, row_bytes)));
+            (FA_LDS s16x4*)(base + tile_offset<CPR>(row, col)));
         const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
@@ -159,7 +150,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
         const int blk = i * kNW + wave, pos = blk * 64 + lane;
         const int row = pos / CH, sw = pos % CH;
         buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
-                        (uint32_t)((j0 + row) * D + ((sw ^ swz(row)) << 3)) * 2);
+                        (uint32_t)((j0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2);
     }
 
     f32x16 dva[DB], dka[DB];
@@ -173,7 +164,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
         for (int i = 0; i < QLOADS; ++i) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
-            const uint32_t off = (uint32_t)((i0 + row) * D + ((sw ^ swz(row)) << 3)) * 2;
+            const uint32_t off = (uint32_t)((i0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2;
             buffer_to_lds16(rs_q, (FA_LDS void*)(qL + blk * 1024), off);
             buffer_to_lds16(rs_do, (FA_LDS void*)(doL + blk * 1024), off);
         }
@@ -199,7 +190,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    *(FA_LDS u32x2*)(dsL + lds_off(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi, BQ * 2)) =
+                    *(FA_LDS u32x2*)(dsL + tile_offset<BQ / 8>(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi)) =
                         u32x2{0u, 0u};
         } else {
             f32x16 s[QB], dp[QB];
@@ -210,9 +201,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
                 for (int c = 0; c < NCD; ++c) {
                     s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        row_operand(qL, D * 2, qb * 32, 16 * c, lane), kt[c], s[qb], 0, 0, 0);
+                        row_operand<CH>(qL, qb * 32, 16 * c, lane), kt[c], s[qb], 0, 0, 0);
                     dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        row_operand(doL, D * 2, qb * 32, 16 * c, lane), vt[c], dp[qb], 0, 0, 0);
+                        row_operand<CH>(doL, qb * 32, 16 * c, lane), vt[c], dp[qb], 0, 0, 0);
                 }
             }
             const bool need_mask = (CAUSAL && i0 < kw + 31) || (kw + 32 > N) || (i0 + BQ > N);
@@ -249,9 +240,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_operand(doL, D * 2, 16 * qc, 32 * db, lane), bp, dva[db], 0, 0, 0);
+                        tr_operand<CH>(doL, 16 * qc, 32 * db, lane), bp, dva[db], 0, 0, 0);
                     dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_operand(qL, D * 2, 16 * qc, 32 * db, lane), bs, dka[db], 0, 0, 0);
+                        tr_operand<CH>(qL, 16 * qc, 32 * db, lane), bs, dka[db], 0, 0, 0);
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
@@ -262,7 +253,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                     u32x2 w;
                     w[0] = pack_bf16x2(dp[qb][4 * g + 0], dp[qb][4 * g + 1]);
                     w[1] = pack_bf16x2(dp[qb][4 * g + 2], dp[qb][4 * g + 3]);
-                    *(FA_LDS u32x2*)(dsL + lds_off(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi, BQ * 2)) = w;
+                    *(FA_LDS u32x2*)(dsL + tile_offset<BQ / 8>(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi)) = w;
                 }
         }
         __syncthreads();
@@ -278,8 +269,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
             for (int kc = 0; kc < kBKV / 16; ++kc)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    tr_operand(dsL, BQ * 2, 16 * kc, 32 * qb, lane),
-                    tr_operand(kL, D * 2, 16 * kc, 32 * db, lane), acc, 0, 0, 0);
+                    tr_operand<BQ / 8>(dsL, 16 * kc, 32 * qb, lane),
+                    tr_operand<CH>(kL, 16 * kc, 32 * db, lane), acc, 0, 0, 0);
             float* dst = p.dq_acc + head + 32 * db + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {

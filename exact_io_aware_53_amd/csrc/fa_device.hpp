@@ -42,6 +42,28 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ------------------------------------------------------------- LDS swizzle
+// gfx950 LDS serves 256 bytes per pass: 16 lanes of a 16-byte read, or 32
+// lanes of an 8-byte transposed read. Tiles are stored row-major with their
+// 16-byte chunks XOR-permuted per row so that both access shapes used by the
+// matrix-core operands hit 16 distinct 16-byte bank groups:
+//   * 16 consecutive rows, same chunk (row operands, ds_read_b128);
+//   * 4 aligned rows x 64 contiguous bytes (ds_read_b64_tr_b16 of a 32-wide
+//     column block by lanes 0-31).
+// CPR = 16-byte chunks per row (8 for 128-byte rows, 16 for 256-byte rows).
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+    static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
+    if (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Byte offset of element (row, col) of a bf16 tile with CPR chunks per row.
+template <int CPR>
+__device__ __forceinline__ int tile_offset(int row, int col) {
+    return row * CPR * 16 + (((col >> 3) ^ chunk_swizzle<CPR>(row)) << 4) + ((col & 7) << 1);
+}
+
 // --------------------------------------------------------------- exchange
 // Value held by lane (l ^ 32): v_permlane32_swap exchanges the upper half of
 // the first operand with the lower half of the second, so swapping x with

@@ -22,8 +22,8 @@
 // * K/V tiles travel HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //   staging), double-buffered, with out-of-range rows of a ragged tail
 //   returned as zeros by the buffer range check. Chunks of 16 bytes are
-//   XOR-swizzled per row so that both the K reads (8 rows, same columns) and
-//   the transposed V reads (4 rows x 32 bytes) hit distinct LDS banks.
+//   XOR-swizzled per row (chunk_swizzle) so that both the K reads (16 rows,
+//   same columns) and the transposed V reads hit distinct LDS banks.
 // * The scale is applied in fp32 after the product and folded with log2(e)
 //   into the exp2 argument: p = exp2(s * c - m2) with c = scale * log2(e) and
 //   m2 the running maximum of s * c. The division by l (and by 1 - p_drop)
@@ -40,6 +40,13 @@
 namespace fa {
 namespace {
 
+// Slack, in log2 units, by which a tile maximum may exceed the reference
+// maximum before the accumulators are rescaled. Zero keeps the reference equal
+// to the true running maximum (the recurrence as printed), so the key that
+// attains a row's maximum gets P~ = 1 exactly, with no bf16 rounding on the
+// dominant term of a peaked row; a positive slack lets that term round.
+constexpr float RESCALE_SLACK = 0.0f;
+
 struct FwdParamsB {
     const __bf16* q;
     const __bf16* k;
@@ -53,12 +60,14 @@ struct FwdParamsB {
     PhiloxKey key;
 };
 
-// 16-byte chunk swizzles inside one row of a K or V tile.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// LDS operand reads kept in flight ahead of the matrix-core product that uses them.
+#ifndef FA_FWD_PREFETCH
+#define FA_FWD_PREFETCH 3
+#endif
+constexpr int kPrefetch = FA_FWD_PREFETCH;
 
 template <int D, int BC, int NW, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParamsB p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParamsB p) {
     constexpr int BR = NW * 32;            // query rows per workgroup
     constexpr int CH = D / 8;              // 16-byte chunks per row
     constexpr int KB = BC / 32;            // 32-key blocks per tile
@@ -67,8 +76,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParamsB p) {
     constexpr int TILE_BYTES = BC * D * 2;
     constexpr int LOADS = BC * CH / (64 * NW);   // 16-byte loads per lane per tensor per tile
     static_assert(LOADS * 64 * NW == BC * CH, "tile must split evenly over the waves");
+    constexpr int S_MFMA = KB * (D / 16);  // products of one score tile
+    constexpr int PV_MFMA = NC * DB;       // products of one PV update
+    constexpr int E = KB * 16;             // score elements per lane
+    // Slots of the interleaved score/softmax sequence: the row maximum is
+    // spread over the first MAX_SLOTS products, one slot exchanges it across
+    // the half-waves, and the exponentials fill the remaining EXP_SLOTS.
+    constexpr int MAX_SLOTS = S_MFMA >= 8 ? S_MFMA / 4 : 1;
+    constexpr int EXP_SLOTS = S_MFMA - MAX_SLOTS - 1;
+    static_assert(EXP_SLOTS >= 1, "too few products to interleave the softmax");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE_BYTES];   // [buffer][K, V]
+    __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];   // two K tiles
+    __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];   // two V tiles
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -112,142 +131,242 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParamsB p) {
     for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-    float m2 = -INFINITY;   // running max of s * c for row my_q (same in both half-waves)
+    float m2 = -INFINITY;   // reference maximum of s * c for row my_q (same in both half-waves)
     float lsum = 0.0f;      // this lane's share of the running denominator
 
     const int last_q = min(N, q0 + BR) - 1;
     const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
+    // Tiles this wave needs: causal rows stop at their diagonal; rows past N need none.
+    const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + 31, N - 1) / BC + 1) : ntiles;
 
-    auto issue_tile = [&](int t, int buf) {
+    auto kl = [&](int i) { return (FA_LDS char*)kbuf + i * TILE_BYTES; };
+    auto vl = [&](int i) { return (FA_LDS char*)vbuf + i * TILE_BYTES; };
+
+    // HBM -> LDS copy of rows [t*BC, t*BC + BC) of K or V, chunks swizzled per row.
+    auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int t, FA_LDS char* dst) {
         const int k0 = t * BC;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int blk = i * NW + wave;             // 1 KB block of the tile written by this wave
             const int pos = blk * 64 + lane;           // 16-byte slot in the tile
             const int row = pos / CH, sw = pos % CH;
-            const uint32_t base = (uint32_t)(k0 + row) * D;
-            buffer_to_lds16(rs_k, (FA_LDS void*)(&smem[buf][0][blk * 1024]),
-                            (base + (uint32_t)((sw ^ swz_k(row)) * 8)) * 2);
-            buffer_to_lds16(rs_v, (FA_LDS void*)(&smem[buf][1][blk * 1024]),
-                            (base + (uint32_t)((sw ^ swz_v(row)) * 8)) * 2);
+            const uint32_t off = ((uint32_t)(k0 + row) * D + (uint32_t)((sw ^ chunk_swizzle<CH>(row)) * 8)) * 2;
+            buffer_to_lds16(rs, (FA_LDS void*)(dst + blk * 1024), off);
         }
     };
 
-    issue_tile(0, 0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-
-        const int k0 = t * BC;
-        if (CAUSAL && k0 > qw + 31) continue;      // whole tile above the diagonal for this wave
-
-        const FA_LDS char* kt = (const FA_LDS char*)smem[buf][0];
-        const FA_LDS char* vt = (const FA_LDS char*)smem[buf][1];
-
-        // ---- S^T = K Q^T for KB blocks of 32 keys
-        f32x16 s[KB];
+    // S^T = K Q^T for KB blocks of 32 keys. Element (kb, r) of a lane is key
+    // row 32kb + 8(r/4) + 4hi + r%4 of the tile against query row my_q.
+    auto score_tile = [&](f32x16 (&s)[KB], const FA_LDS char* kt) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-            const int row = kb * 32 + l32;
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const int chunk = (2 * c + hi) ^ swz_k(row);
-                const bf16x8 a = *(const FA_LDS bf16x8*)(kt + row * D * 2 + chunk * 16);
+        for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 a = *(const FA_LDS bf16x8*)(kt + tile_offset<CH>(kb * 32 + l32, 16 * c + 8 * hi));
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], s[kb], 0, 0, 0);
             }
-        }
+    };
 
-        // ---- mask (diagonal / ragged tiles only). Element (kb, r): key row
-        // 32kb + 8(r/4) + 4hi + r%4 of the tile, query row my_q.
-        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
-        if (need_mask) {
+    // K operand of score product i (i = c * KB + kb): key row 32kb + l32, d = 16c + 8hi .. +7.
+    auto k_operand = [&](const FA_LDS char* kt, int i) {
+        const int kb = i % KB, c = i / KB;
+        return *(const FA_LDS bf16x8*)(kt + tile_offset<CH>(kb * 32 + l32, 16 * c + 8 * hi));
+    };
+
+    // V^T operand of PV product j (j = c * DB + db): lane holds d = 32db + l32
+    // and keys 16c + 4hi + {0..3} (first read) and 16c + 8 + 4hi + {0..3}
+    // (second read). Within a 16-lane group, lane s of the transposed read
+    // addresses key (s / 4) and columns 4 (s % 4) .. +3 of its 4x16 block.
+    const int grp = lane >> 4, sl = lane & 15;
+    const int vd = 16 * (grp & 1) + 4 * (sl & 3);      // column inside the 32-wide d block
+    auto v_operand = [&](const FA_LDS char* vt, int j) {
+        const int c = j / DB, db = j % DB;
+        bf16x8 a;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+        for (int half = 0; half < 2; ++half) {
+            const int key = 16 * c + 8 * half + 4 * (grp >> 1) + (sl >> 2);
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (FA_LDS s16x4*)(vt + tile_offset<CH>(key, 32 * db + vd)));
+            const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool dead = (CAUSAL && key > my_q) || key >= N;
-                    if (dead) s[kb][r] = -INFINITY;
+            for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
+        }
+        return a;
+    };
+
+    // Next score tile on the matrix cores interleaved, product by product,
+    // with this tile's softmax on the vector ALUs (no dropout). The order is
+    // fixed with scheduling fences; K operands are read kPrefetch products
+    // ahead so the LDS latency stays hidden.
+    auto score_and_softmax = [&](f32x16 (&sn)[KB], const FA_LDS char* kt, f32x16 (&s)[KB],
+                                 bf16x8 (&pb)[NC], float& m_new, float& tsum) {
+        bf16x8 kop[kPrefetch];
+#pragma unroll
+        for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand(kt, j);
+        float mx = -INFINITY, neg = 0.0f;
+        tsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < S_MFMA; ++i) {
+            const int kb = i % KB, c = i / KB;
+            if (c == 0)
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[0], f32x16{}, 0, 0, 0);
+            else
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[c], sn[kb], 0, 0, 0);
+            if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand(kt, i + kPrefetch);
+            if (i < MAX_SLOTS) {
+#pragma unroll
+                for (int e = i * E / MAX_SLOTS; e < (i + 1) * E / MAX_SLOTS; ++e)
+                    mx = fmaxf(mx, s[e / 16][e % 16]);
+            } else if (i == MAX_SLOTS) {
+                mx = max_with_partner32(mx) * p.sl2;
+                m_new = fmaxf(m2, mx);
+                neg = -m_new;
+            } else {
+                const int j = i - MAX_SLOTS - 1;
+                const int e0 = ((j * E) / EXP_SLOTS) & ~1, e1 = (((j + 1) * E) / EXP_SLOTS) & ~1;
+#pragma unroll
+                for (int e = e0; e < e1; e += 2) {
+                    const float x0 = fast_exp2(fmaf(s[e / 16][e % 16], p.sl2, neg));
+                    const float x1 = fast_exp2(fmaf(s[e / 16][e % 16 + 1], p.sl2, neg));
+                    tsum += x0;
+                    tsum += x1;
+                    const int pc = (e / 16) * 2 + (e % 16) / 8, pi = e % 8;
+                    pb[pc][pi] = (__bf16)x0;
+                    pb[pc][pi + 1] = (__bf16)x1;
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
 
-        // ---- online softmax (log2 domain)
+    // Online softmax of one score tile (log2 domain): row maximum against the
+    // reference m2, P~ = exp2(s*c - m_new) with its row sum, dropout, and the
+    // bf16 B operands of the PV product. O~ and l are rescaled afterwards.
+    auto softmax = [&](f32x16 (&s)[KB], bf16x8 (&pb)[NC], float& m_new, float& tsum, int k0) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_with_partner32(mx);
-        const float m_new = fmaxf(m2, mx * p.sl2);
-        const float alpha = fast_exp2(m2 - m_new);   // exp2(-inf) = 0 on the first tile
-        const float neg = -m_new;
-        float tsum = 0.0f;
+        mx = max_with_partner32(mx) * p.sl2;
+        m_new = fmaxf(m2, mx);
+        // dropout keep bits, bit r of word kb for element (kb, r)
+        uint32_t keep[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(fmaf(s[kb][r], p.sl2, neg));
-                s[kb][r] = e;
-                tsum += e;
-            }
-        lsum = fmaf(lsum, alpha, tsum);
-        m2 = m_new;
-
-        if (DROPOUT) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            keep[kb] = 0xffffu;
+            if (DROPOUT) {
+                uint32_t bits = 0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                     const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)my_q,
                                                     (uint32_t)key, p.key);
-                    if (w < p.thr) s[kb][r] = 0.0f;
+                    bits |= (uint32_t)(w >= p.thr) << r;
                 }
+                keep[kb] = bits;
+            }
         }
-
-        // ---- P^T chunks as bf16 B operands: chunk c = 16 keys, regs 8*(c%2) .. +7 of block c/2
-        bf16x8 pb[NC];
+        const float neg = -m_new;
+        tsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(fmaf(s[kb][r], p.sl2, neg));
+                tsum += e;
+                s[kb][r] = DROPOUT ? ((keep[kb] >> r) & 1u ? e : 0.0f) : e;
+            }
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int i = 0; i < 8; ++i) pb[c][i] = (__bf16)s[c >> 1][8 * (c & 1) + i];
+    };
 
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    // One key/value tile: wait for K_{t+1} and V_t, refill the buffers freed
+    // by the previous step (V_{t+1}, K_{t+2}), then overlap the next score
+    // tile on the matrix cores with this tile's softmax on the vector ALUs,
+    // and finish with O~ += V_t^T P_t^T.
+    auto step = [&](f32x16 (&sc)[KB], f32x16 (&sn)[KB], int t) {
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < ntiles) issue(rs_v, t + 1, vl((t + 1) & 1));
+        if (t + 2 < ntiles) issue(rs_k, t + 2, kl(t & 1));
+        if (t >= ntiles_w) return;
 
-        // ---- O^T += V^T P^T. A operand for (db, c): lane holds d = 32db + l32
-        // and keys 16c + 4hi + {0..3} (first read) and 16c + 8 + 4hi + {0..3}
-        // (second read). Within a 16-lane group, lane s of the transposed read
-        // addresses key (s / 4) and columns 4 (s % 4) .. +3 of its 4x16 block.
-        const int grp = lane >> 4, sl = lane & 15;
-        const int vd = 16 * (grp & 1) + 4 * (sl & 3);      // column inside the 32-wide d block
+        const int k0 = t * BC;
+        // mask: only tiles that cross the diagonal or the ragged end
+        if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N)) {
+            const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                bf16x8 a;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int key = 16 * c + 8 * half + 4 * (grp >> 1) + (sl >> 2);
-                    const int d = 32 * db + vd;
-                    const int chunk = (d >> 3) ^ swz_v(key);
-                    const FA_LDS s16x4* src =
-                        (const FA_LDS s16x4*)(vt + key * D * 2 + chunk * 16 + (d & 7) * 2);
-                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)src);
-                    const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    sc[kb][r] = key > lim ? -INFINITY : sc[kb][r];
                 }
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
-            }
         }
+
+        bf16x8 pb[NC];
+        float m_new, tsum;
+        if (t + 1 < ntiles_w) {
+            if (DROPOUT) {
+                // the dropout generator's long integer chains dominate; the
+                // default schedule overlaps them with the products
+                score_tile(sn, kl((t + 1) & 1));
+                softmax(sc, pb, m_new, tsum, k0);
+            } else {
+                score_and_softmax(sn, kl((t + 1) & 1), sc, pb, m_new, tsum);
+            }
+        } else {
+            softmax(sc, pb, m_new, tsum, k0);
+        }
+
+        // Rescale only when some row of the wave raised its maximum (by more
+        // than RESCALE_SLACK); otherwise every factor would be exactly 1.
+        if (__builtin_amdgcn_ballot_w64(m_new > m2 + RESCALE_SLACK)) {
+            const float alpha = fast_exp2(m2 - m_new);   // exp2(-inf) = 0 on the first tile
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        m2 = m_new;
+        lsum += tsum;
+
+        // O~^T += V^T P^T, V^T operands read kPrefetch products ahead
+        const FA_LDS char* vt = vl(t & 1);
+        bf16x8 vop[kPrefetch];
+#pragma unroll
+        for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand(vt, j);
+#pragma unroll
+        for (int j = 0; j < PV_MFMA; ++j) {
+            const int c = j / DB, db = j % DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[c], oacc[db], 0, 0, 0);
+            if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand(vt, j + kPrefetch);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- prologue: K_0, V_0, K_1 resident, first score tile
+    issue(rs_k, 0, kl(0));
+    issue(rs_v, 0, vl(0));
+    if (ntiles > 1) issue(rs_k, 1, kl(1));
+    wait_vmem();
+    __syncthreads();
+    f32x16 sa[KB], sb[KB];
+    if (ntiles_w > 0) score_tile(sa, kl(0));
+
+    // Two steps per trip so the current and next score tiles swap roles
+    // without register copies.
+    for (int t = 0; t < ntiles; t += 2) {
+        step(sa, sb, t);
+        if (t + 1 < ntiles) step(sb, sa, t + 1);
     }
 
     // ---- epilogue: O = O~ / (l (1 - p)), LSE = (m2 + log2 l) ln 2
@@ -268,9 +387,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParamsB p) {
     }
 }
 
+// Keys per K/V tile and waves (32 query rows each) per workgroup.
+#ifndef FA_FWD_BC
+#define FA_FWD_BC 64
+#endif
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 4
+#endif
+
 template <int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-    constexpr int BC = 64, NW = 4, BR = NW * 32;
+    constexpr int BC = FA_FWD_BC, NW = FA_FWD_NW, BR = NW * 32;
     FwdParamsB p{};
     p.q = (const __bf16*)a.q;
     p.k = (const __bf16*)a.k;
