@@ -109,12 +109,14 @@ def cpu_baseline(w, inputs, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-bwd", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB copy kernel (for HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -204,6 +206,16 @@ def main():
             "tflops_fwd_bwd": round((w2.fwd_flops() + w2.bwd_flops()) / ((tf + tb) * 1e-3) / 1e12, 3),
         }
         del q2, k2, v2, do2, o2, l2, dq2, dk2, dv2, ws
+
+    if args.calibrate_copy:
+        # A plain elementwise copy of known size: reads and writes 2^30 bytes per launch.
+        src = torch.ones(2**28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = 2**30
+        del src, dst
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget)

@@ -62,7 +62,7 @@ struct FwdParamsB {
 
 // LDS operand reads kept in flight ahead of the matrix-core product that uses them.
 #ifndef FA_FWD_PREFETCH
-#define FA_FWD_PREFETCH 3
+#define FA_FWD_PREFETCH 2
 #endif
 constexpr int kPrefetch = FA_FWD_PREFETCH;
 
@@ -387,6 +387,268 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
+// Two-group ("ping-pong") form of the same forward pass. Eight waves share
+// each K/V tile: waves 0-3 (group A) own query rows [q0, q0+128) and waves
+// 4-7 (group B) rows [q0+128, q0+256); wave w and wave w+4 share one SIMD.
+// A group alternates a matrix-core phase M(t) = {O~ += V_{t-1}^T P_{t-1}^T,
+// S_t = K_t Q^T} with a vector-ALU phase V(t) = softmax of S_t. Group B runs
+// one phase behind group A and a workgroup barrier closes every phase, so on
+// each SIMD one wave feeds the matrix core while the other runs its softmax.
+//
+//   interval:   0      1      2      3      4    ...
+//   group A:   M(0)   V(0)   M(1)   V(1)   M(2)
+//   group B:    -     M(0)   V(0)   M(1)   V(1)
+//
+// K_t and V_{t-1} are read in intervals 2t and 2t+1. K_{t+1} and V_t are
+// fetched at the start of interval 2t into the buffers last read in interval
+// 2t-1, and waited for at the end of interval 2t+1.
+template <int D, int BC, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pingpong_kernel(FwdParamsB p) {
+    constexpr int NW = 8, BR = 256;
+    constexpr int CH = D / 8, KB = BC / 32, NC = BC / 16, DB = D / 32;
+    constexpr int TILE_BYTES = BC * D * 2;
+    constexpr int LOADS = BC * CH / (64 * NW);
+    static_assert(LOADS * 64 * NW == BC * CH, "tile must split evenly over the waves");
+    constexpr int S_MFMA = KB * (D / 16), PV_MFMA = NC * DB;
+
+    __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const bool group_b = wave >= 4;
+
+    int bh, qb;
+    const int bid = blockIdx.x;
+    if ((p.heads & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        bh = (slot / p.nqb) * 8 + xcd;
+        qb = slot % p.nqb;
+    } else {
+        bh = bid % p.heads;
+        qb = bid / p.heads;
+    }
+    if (CAUSAL) qb = p.nqb - 1 - qb;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int N = p.N;
+    const size_t head = (size_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const auto rs_q = make_rsrc(p.q + head, head_bytes);
+    const auto rs_k = make_rsrc(p.k + head, head_bytes);
+    const auto rs_v = make_rsrc(p.v + head, head_bytes);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + wave * 32;
+    const int my_q = qw + l32;
+
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        qreg[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_q, (uint32_t)(my_q * D + 16 * c + 8 * hi) * 2));
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+    float m2 = -INFINITY, lsum = 0.0f;
+
+    const int last_q = min(N, q0 + BR) - 1;
+    const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
+    const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + 31, N - 1) / BC + 1) : ntiles;
+
+    auto kl = [&](int i) { return (FA_LDS char*)kbuf + i * TILE_BYTES; };
+    auto vl = [&](int i) { return (FA_LDS char*)vbuf + i * TILE_BYTES; };
+    auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int t, FA_LDS char* dst) {
+        const int k0 = t * BC;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int blk = i * NW + wave, pos = blk * 64 + lane;
+            const int row = pos / CH, sw = pos % CH;
+            const uint32_t off = ((uint32_t)(k0 + row) * D + (uint32_t)((sw ^ chunk_swizzle<CH>(row)) * 8)) * 2;
+            buffer_to_lds16(rs, (FA_LDS void*)(dst + blk * 1024), off);
+        }
+    };
+    // Per-lane LDS byte offsets of the operand reads. A K read (product i =
+    // c*KB + kb) is koff[c] + kb*32 rows; a V^T read (product j = c*DB + db,
+    // half) is voff[db][half] + 16c rows: the swizzle depends only on the low
+    // row bits, so the row-block terms are plain immediate offsets.
+    constexpr int ROW_BYTES = CH * 16;
+    int koff[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) koff[c] = tile_offset<CH>(l32, 16 * c + 8 * hi);
+    const int grp = lane >> 4, sl = lane & 15;
+    const int vd = 16 * (grp & 1) + 4 * (sl & 3);
+    int voff[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+            voff[db][half] = tile_offset<CH>(8 * half + 4 * (grp >> 1) + (sl >> 2), 32 * db + vd);
+    auto k_operand = [&](const FA_LDS char* kt, int i) {
+        const int kb = i % KB, c = i / KB;
+        return *(const FA_LDS bf16x8*)(kt + koff[c] + kb * 32 * ROW_BYTES);
+    };
+    auto v_operand = [&](const FA_LDS char* vt, int j) {
+        const int c = j / DB, db = j % DB;
+        bf16x8 a;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (FA_LDS s16x4*)(vt + voff[db][half] + 16 * c * ROW_BYTES));
+            const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
+        }
+        return a;
+    };
+
+    f32x16 s[KB];
+    bf16x8 pb[NC];
+
+    // M(t): O~ += V_{t-1}^T P_{t-1}^T and S_t = K_t Q^T, operands read kPrefetch ahead.
+    auto matrix_phase = [&](int t) {
+        const bool do_pv = t >= 1 && t - 1 < ntiles_w;
+        const bool do_s = t < ntiles_w;
+        if (do_pv) {
+            const FA_LDS char* vt = vl((t - 1) & 1);
+            bf16x8 vop[kPrefetch];
+#pragma unroll
+            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand(vt, j);
+#pragma unroll
+            for (int j = 0; j < PV_MFMA; ++j) {
+                oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[j / DB], oacc[j % DB], 0, 0, 0);
+                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand(vt, j + kPrefetch);
+            }
+        }
+        if (do_s) {
+            const FA_LDS char* kt = kl(t & 1);
+            bf16x8 kop[kPrefetch];
+#pragma unroll
+            for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand(kt, j);
+#pragma unroll
+            for (int i = 0; i < S_MFMA; ++i) {
+                const int kb = i % KB, c = i / KB;
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[c],
+                                                                c == 0 ? f32x16{} : s[kb], 0, 0, 0);
+                if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand(kt, i + kPrefetch);
+            }
+        }
+    };
+
+    // V(t): mask, online softmax of S_t (log2 domain), dropout, P_t as bf16
+    // B operands, and the rescale of O~ and l when a row maximum grew.
+    auto vector_phase = [&](int t) {
+        if (t >= ntiles_w) return;
+        const int k0 = t * BC;
+        if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N)) {
+            const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_with_partner32(mx) * p.sl2;
+        const float m_new = fmaxf(m2, mx);
+        uint32_t keep[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            keep[kb] = 0xffffu;
+            if (DROPOUT) {
+                uint32_t bits = 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)my_q,
+                                                    (uint32_t)key, p.key);
+                    bits |= (uint32_t)(w >= p.thr) << r;
+                }
+                keep[kb] = bits;
+            }
+        }
+        const float neg = -m_new;
+        float tsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float x0 = fast_exp2(fmaf(s[kb][r], p.sl2, neg));
+                const float x1 = fast_exp2(fmaf(s[kb][r + 1], p.sl2, neg));
+                tsum += x0;
+                tsum += x1;
+                const int pc = kb * 2 + r / 8, pi = r % 8;
+                pb[pc][pi] = (__bf16)(DROPOUT ? ((keep[kb] >> r) & 1u ? x0 : 0.0f) : x0);
+                pb[pc][pi + 1] = (__bf16)(DROPOUT ? ((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f) : x1);
+            }
+        if (__builtin_amdgcn_ballot_w64(m_new > m2 + RESCALE_SLACK)) {
+            const float alpha = fast_exp2(m2 - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        m2 = m_new;
+        lsum += tsum;
+    };
+
+    // prologue: K_0 resident before interval 0
+    issue(rs_k, 0, kl(0));
+    wait_vmem();
+    __syncthreads();
+
+    // Interval 2t starts by fetching K_{t+1} and V_t; interval 2t+1 ends by
+    // waiting for them. Each group runs its own loop with the same barriers.
+    auto fetch = [&](int t) {
+        if (t + 1 < ntiles) issue(rs_k, t + 1, kl((t + 1) & 1));
+        if (t < ntiles) issue(rs_v, t, vl(t & 1));
+    };
+    if (!group_b) {
+        for (int t = 0; t <= ntiles; ++t) {
+            fetch(t);
+            matrix_phase(t);
+            __syncthreads();
+            vector_phase(t);
+            wait_vmem();
+            __syncthreads();
+        }
+    } else {
+        for (int t = 0; t <= ntiles; ++t) {
+            fetch(t);
+            if (t >= 1) vector_phase(t - 1);
+            __syncthreads();
+            matrix_phase(t);
+            wait_vmem();
+            __syncthreads();
+        }
+    }
+
+    const float ltot = add_with_partner32(lsum);
+    const float inv = p.inv_keep / ltot;
+    if (my_q < N) {
+        __bf16* orow = p.o + head + (size_t)my_q * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (__bf16)(oacc[db][4 * g + i] * inv);
+                *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
+            }
+        if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m2 + fast_log2(ltot)) * kLn2;
+    }
+}
+
 // Keys per K/V tile and waves (32 query rows each) per workgroup.
 #ifndef FA_FWD_BC
 #define FA_FWD_BC 64
@@ -395,9 +657,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #define FA_FWD_NW 4
 #endif
 
+// The two-group form is kept for measurement; on gfx950 the matrix cores and
+// the vector ALUs of a SIMD do not run concurrently (measured: their cycle
+// counts add), so it does not beat the single-group form.
+#ifndef FA_FWD_PINGPONG
+#define FA_FWD_PINGPONG 0
+#endif
+
 template <int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-    constexpr int BC = FA_FWD_BC, NW = FA_FWD_NW, BR = NW * 32;
+    constexpr bool PP = FA_FWD_PINGPONG;
+    constexpr int BC = FA_FWD_BC, NW = PP ? 8 : FA_FWD_NW, BR = NW * 32;
     FwdParamsB p{};
     p.q = (const __bf16*)a.q;
     p.k = (const __bf16*)a.k;
@@ -412,8 +682,12 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
     p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, CAUSAL, DROPOUT>), dim3(p.heads * p.nqb),
-                       dim3(NW * 64), 0, st, p);
+    if (PP)
+        hipLaunchKernelGGL((fwd_pingpong_kernel<D, BC, CAUSAL, DROPOUT>), dim3(p.heads * p.nqb),
+                           dim3(NW * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, CAUSAL, DROPOUT>), dim3(p.heads * p.nqb),
+                           dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
