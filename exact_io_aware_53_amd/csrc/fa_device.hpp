@@ -105,22 +105,88 @@ struct PhiloxKey {
     uint32_t k0, k1;
 };
 
+// a ^ b ^ k in one v_bitop3_b32 (truth table 0x96); k is wave-uniform.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+    return r;
+}
+
+// One round on counter (c0, c1, c2, c3) with round key (k0, k1). The 32x32->64
+// products are plain 64-bit multiplies (one v_mad_u64_u32 each on gfx950).
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                             uint32_t k0, uint32_t k1) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+}
+
 // Output word 0 of the block function at counter (c0, c1, c2, c3).
 __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  PhiloxKey key) {
     uint32_t k0 = key.k0, k1 = key.k1;
 #pragma unroll
     for (int r = 0; r < 9; ++r) {
-        const uint32_t hi0 = __umulhi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
-        const uint32_t hi1 = __umulhi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
-        c0 = hi1 ^ c1 ^ k0;
-        c1 = lo1;
-        c2 = hi0 ^ c3 ^ k1;
-        c3 = lo0;
+        philox_round(c0, c1, c2, c3, k0, k1);
         k0 += kPhiloxW0;
         k1 += kPhiloxW1;
     }
-    return __umulhi(kPhiloxM1, c2) ^ c1 ^ k0;   // round 10, word 0 only
+    return xor3((uint32_t)(((uint64_t)kPhiloxM1 * c2) >> 32), c1, k0);   // round 10, word 0 only
 }
+
+// Word 0 at counter (c0, c1, c2, j) for a fixed (c0, c1, c2) and varying j:
+// the parts of rounds 1-3 that do not depend on j are computed once.
+//   round 1: x0, x1, x3 fixed; x2 = A ^ j
+//   round 2: y0 = hi(M1 x2) ^ B, y1 = lo(M1 x2); y2, y3 fixed
+//   round 3: z0 = D0 ^ y1, z1 = E1 fixed, z2 = hi(M0 y0) ^ F, z3 = lo(M0 y0)
+struct PhiloxRow {
+    uint32_t A, B, D0, E1, F;
+    uint32_t k0_3, k1_3;   // key of round 4
+
+    __device__ __forceinline__ PhiloxRow(uint32_t c0, uint32_t c1, uint32_t c2, PhiloxKey key) {
+        uint32_t k0 = key.k0, k1 = key.k1;
+        const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;   // round 1
+        const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+        const uint32_t x0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t x1 = (uint32_t)p1;
+        const uint32_t x3 = (uint32_t)p0;
+        A = (uint32_t)(p0 >> 32) ^ k1;
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+        const uint64_t q0 = (uint64_t)kPhiloxM0 * x0;   // round 2, fixed half
+        B = x1 ^ k0;
+        const uint32_t y2 = (uint32_t)(q0 >> 32) ^ x3 ^ k1;
+        const uint32_t y3 = (uint32_t)q0;
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+        const uint64_t r1 = (uint64_t)kPhiloxM1 * y2;   // round 3, fixed half
+        D0 = (uint32_t)(r1 >> 32) ^ k0;
+        E1 = (uint32_t)r1;
+        F = y3 ^ k1;
+        k0_3 = k0 + kPhiloxW0;
+        k1_3 = k1 + kPhiloxW1;
+    }
+
+    __device__ __forceinline__ uint32_t word0(uint32_t j) const {
+        const uint64_t q1 = (uint64_t)kPhiloxM1 * (A ^ j);   // round 2, varying half
+        const uint32_t y0 = (uint32_t)(q1 >> 32) ^ B;
+        const uint32_t y1 = (uint32_t)q1;
+        const uint64_t r0 = (uint64_t)kPhiloxM0 * y0;       // round 3, varying half
+        uint32_t c0 = D0 ^ y1, c1 = E1, c2 = (uint32_t)(r0 >> 32) ^ F, c3 = (uint32_t)r0;
+        uint32_t k0 = k0_3, k1 = k1_3;
+#pragma unroll
+        for (int r = 3; r < 9; ++r) {
+            philox_round(c0, c1, c2, c3, k0, k1);
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        return xor3((uint32_t)(((uint64_t)kPhiloxM1 * c2) >> 32), c1, k0);
+    }
+};
 
 }  // namespace fa

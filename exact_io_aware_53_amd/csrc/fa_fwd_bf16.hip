@@ -140,6 +140,12 @@ void fwd_bf16_kernel(FwdParamsB p) {
         lbf[rb] = 0.0f;
     }
 
+    // Dropout generator state of each row block's row (counter b, h, row, key).
+    PhiloxRow philox[RB] = {PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + l32), p.key)};
+#pragma unroll
+    for (int rb = 1; rb < RB; ++rb)
+        philox[rb] = PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + 32 * rb + l32), p.key);
+
     const int last_q = min(N, q0 + BR) - 1;
     const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
     // Tiles this wave needs: causal rows stop at their diagonal; rows past N need none.
@@ -270,9 +276,7 @@ void fwd_bf16_kernel(FwdParamsB p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)my_q,
-                                                        (uint32_t)key, p.key);
-                        bits |= (uint32_t)(w >= p.thr) << r;
+                        bits |= (uint32_t)(philox[rb].word0((uint32_t)key) >= p.thr) << r;
                     }
                     keep[kb] = bits;
                 }
