@@ -96,6 +96,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     constexpr int KLOADS = kBKV * CH / (64 * kNW);
     static_assert(QLOADS * 64 * kNW == BQ * CH, "query tile must split over the waves");
     static_assert(BQ == 64, "dS^T rows need 8 chunks for the swizzle");
+    static_assert((QB * DB) % kNW == 0, "dQ blocks must split evenly over the waves");
+    constexpr int DQ_ATOMICS = (QB * DB / kNW) * 16;   // dQ atomics per lane per tile
+    static_assert(DQ_ATOMICS <= 63, "vmcnt holds at most 63");
 
     __shared__ __attribute__((aligned(1024))) char q_s[TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[TILE];
@@ -121,6 +124,10 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
         bh = bid % p.heads;
         kb = bid / p.heads;
     }
+    // Workgroup-uniform by construction; stated explicitly so that the buffer
+    // descriptors below live in SGPRs.
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    kb = __builtin_amdgcn_readfirstlane(kb);
     const int b = bh / p.H, h = bh - b * p.H;
     const int N = p.N;
     const size_t head = (size_t)bh * N * D;
@@ -131,6 +138,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     const auto rs_do = make_rsrc(p.dout + head, head_bytes);
     const auto rs_lse = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
     const auto rs_ds = make_rsrc(p.dsum + (size_t)bh * N, (uint32_t)N * 4);
+    // dQ accumulator of the head; atomics at rows >= N fall outside and are dropped.
+    const auto rs_dq = make_rsrc(p.dq_acc + head, (uint32_t)N * D * 4);
 
     const int j0 = kb * kBKV;
     const int kw = j0 + wave * 32;     // first key of this wave
@@ -180,7 +189,13 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     if (i_begin < N) issue_tile(i_begin);
 
     for (int i0 = i_begin; i0 < N; i0 += BQ) {
-        wait_vmem();
+        // Vector-memory operations retire in issue order, and the previous tile
+        // issued this tile's loads before exactly DQ_ATOMICS atomics per lane:
+        // waiting until at most that many remain waits for the loads only.
+        if (i0 == i_begin)
+            wait_vmem();
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DQ_ATOMICS) : "memory");
         __syncthreads();
 
         const bool skip = CAUSAL && kw > i0 + BQ - 1;    // every query of the tile precedes our keys
@@ -271,11 +286,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     tr_operand<BQ / 8>(dsL, 16 * kc, 32 * qb, lane),
                     tr_operand<CH>(kL, 16 * kc, 32 * db, lane), acc, 0, 0, 0);
-            float* dst = p.dq_acc + head + 32 * db + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (qi < N) atomicAdd(dst + (size_t)qi * D, acc[r] * p.scale);
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                    acc[r] * p.scale, rs_dq, (uint32_t)(qi * D + 32 * db + l32) * 4, 0, 0);
             }
         }
     }
