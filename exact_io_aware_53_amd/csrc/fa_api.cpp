@@ -35,7 +35,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(int B, int H, int N, int d) {
     const size_t rows = (size_t)B * H * N;
-    return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+    return round256(rows * d * sizeof(float)) + 2 * round256(rows * sizeof(float));
 }
 
 int map_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -73,8 +73,9 @@ int bwd_common(bool bf16, const void* q, const void* k, const void* v, const voi
     const size_t rows = (size_t)B * H * N;
     float* dq_acc = (float*)workspace;
     float* dsum = (float*)((char*)workspace + round256(rows * d * sizeof(float)));
+    float* lse2 = (float*)((char*)dsum + round256(rows * sizeof(float)));
     fa::BwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, dout, lse,
-                  dq, dk, dv, dq_acc, dsum};
+                  dq, dk, dv, dq_acc, dsum, lse2};
     hipStream_t s = (hipStream_t)stream;
     return map_hip(bf16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }

@@ -45,7 +45,7 @@ struct BwdParamsB {
     const __bf16* k;
     const __bf16* v;
     const __bf16* dout;
-    const float* lse;
+    const float* lse2;     // LSE_i * log2(e), written by the pre-pass
     const float* dsum;
     float* dq_acc;
     __bf16* dk;
@@ -56,31 +56,18 @@ struct BwdParamsB {
     PhiloxKey key;
 };
 
-// Operand whose matrix-core contraction index runs along LDS columns: lane
-// holds row r0 + lane%32, columns c0 + 8*(lane/32) .. +7.
-template <int CPR>
-__device__ __forceinline__ bf16x8 row_operand(const FA_LDS char* base, int r0, int c0, int lane) {
-    const int row = r0 + (lane & 31);
-    const int col = c0 + 8 * (lane >> 5);
-    return *(const FA_LDS bf16x8*)(base + tile_offset<CPR>(row, col));
-}
-
-// Operand whose contraction index runs along LDS rows: lane holds column
-// c0 + lane%32 and rows r0 + 4*(lane/32) + {0..3}, r0 + 8 + 4*(lane/32) + {0..3}
-// (the order in which a 32x32 accumulator holds its rows).
-template <int CPR>
-__device__ __forceinline__ bf16x8 tr_operand(const FA_LDS char* base, int r0, int c0, int lane) {
-    const int grp = lane >> 4, sl = lane & 15;
-    const int col = c0 + 16 * (grp & 1) + 4 * (sl & 3);
+// Transposed matrix-core operand: two ds_read_b64_tr_b16 at per-lane byte
+// offsets off0/off1 (the first and second 8 rows of a 16-row block).
+__device__ __forceinline__ bf16x8 tr_read(const FA_LDS char* base, int off0, int off1) {
+    const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (FA_LDS s16x4*)(base + off0)));
+    const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (FA_LDS s16x4*)(base + off1)));
     bf16x8 a;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int row = r0 + 8 * half + 4 * (grp >> 1) + (sl >> 2);
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS s16x4*)(base + tile_offset<CPR>(row, col)));
-        const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[4 * half + i] = xb[i];
+    for (int i = 0; i < 4; ++i) {
+        a[i] = x0[i];
+        a[4 + i] = x1[i];
     }
     return a;
 }
@@ -136,7 +123,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     const auto rs_k = make_rsrc(p.k + head, head_bytes);
     const auto rs_v = make_rsrc(p.v + head, head_bytes);
     const auto rs_do = make_rsrc(p.dout + head, head_bytes);
-    const auto rs_lse = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+    const auto rs_lse = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4);
     const auto rs_ds = make_rsrc(p.dsum + (size_t)bh * N, (uint32_t)N * 4);
     // dQ accumulator of the head; atomics at rows >= N fall outside and are dropped.
     const auto rs_dq = make_rsrc(p.dq_acc + head, (uint32_t)N * D * 4);
@@ -144,6 +131,28 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     const int j0 = kb * kBKV;
     const int kw = j0 + wave * 32;     // first key of this wave
     const int my_key = kw + l32;
+
+    // Per-lane LDS byte offsets of the operand reads. The chunk swizzle depends
+    // only on the low four row bits, so the 16-row and 32-row block terms added
+    // to these are immediates.
+    //  * row operand (Q, dO as A of S and dP): row l32, d = 16c + 8hi .. +7;
+    //  * transposed operand (Q^T, dO^T, K as the contraction-over-rows side):
+    //    within a 16-lane group, lane s reads row s/4 (+4 for the upper groups,
+    //    +8 for the second read) and 4 columns at 4(s%4) of a 32-wide block;
+    //  * dS^T tile (128-byte rows): the same pattern over query columns.
+    const int grp = lane >> 4, sl = lane & 15;
+    const int tr_row = 4 * (grp >> 1) + (sl >> 2), tr_col = 16 * (grp & 1) + 4 * (sl & 3);
+    int roff[NCD], troff[DB][2], tsoff[QB][2];
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) roff[c] = tile_offset<CH>(l32, 16 * c + 8 * hi);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) troff[db][half] = tile_offset<CH>(tr_row + 8 * half, 32 * db + tr_col);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) tsoff[qb][half] = tile_offset<BQ / 8>(tr_row + 8 * half, 32 * qb + tr_col);
+    }
+    constexpr int ROW = D * 2, SROW = BQ * 2;     // LDS row bytes: Q/dO/K tiles, dS^T tile
 
     // K and V rows of this wave's keys as B operands (d chunk c: d = 16c + 8hi .. +7)
     bf16x8 kt[NCD], vt[NCD];
@@ -185,14 +194,20 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                                                      (uint32_t)(i0 + lane) * 4, 0, 0, 0);
     };
 
-    const int i_begin = CAUSAL ? j0 : 0;
-    if (i_begin < N) issue_tile(i_begin);
+    // Query tiles run from the last one down to the first one this key block
+    // sees. Every key block of a head then starts on the same tile, so the
+    // workgroups of one head that run side by side on an XCD read the same Q
+    // and dO tiles and add into the same dQ rows at about the same time, and
+    // those stay in that XCD's L2.
+    const int i_first = CAUSAL ? j0 : 0;         // j0 < N, so i_first <= i_last
+    const int i_last = (N - 1) / BQ * BQ;
+    issue_tile(i_last);
 
-    for (int i0 = i_begin; i0 < N; i0 += BQ) {
+    for (int i0 = i_last; i0 >= i_first; i0 -= BQ) {
         // Vector-memory operations retire in issue order, and the previous tile
         // issued this tile's loads before exactly DQ_ATOMICS atomics per lane:
         // waiting until at most that many remain waits for the loads only.
-        if (i0 == i_begin)
+        if (i0 == i_last)
             wait_vmem();
         else
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DQ_ATOMICS) : "memory");
@@ -215,24 +230,37 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                 for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.0f;
 #pragma unroll
                 for (int c = 0; c < NCD; ++c) {
+                    const int o = roff[c] + qb * 32 * ROW;
                     s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        row_operand<CH>(qL, qb * 32, 16 * c, lane), kt[c], s[qb], 0, 0, 0);
+                        *(const FA_LDS bf16x8*)(qL + o), kt[c], s[qb], 0, 0, 0);
                     dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        row_operand<CH>(doL, qb * 32, 16 * c, lane), vt[c], dp[qb], 0, 0, 0);
+                        *(const FA_LDS bf16x8*)(doL + o), vt[c], dp[qb], 0, 0, 0);
                 }
             }
-            const bool need_mask = (CAUSAL && i0 < kw + 31) || (kw + 32 > N) || (i0 + BQ > N);
+            // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[qb][r] = fmaf(s[qb][r], p.sl2, -lse_s[qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)]);
+            // Only tiles that cross the diagonal or a ragged end hold masked elements.
+            if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        const bool live = qi < N && my_key < N && (!CAUSAL || my_key <= qi);
+                        if (!live) s[qb][r] = -INFINITY;
+                    }
+            }
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int qrow = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                     const int qi = i0 + qrow;
-                    float pr = fast_exp2(fmaf(s[qb][r], p.sl2, -lse_s[qrow] * kLog2e));
-                    if (need_mask) {
-                        const bool live = qi < N && my_key < N && (!CAUSAL || my_key <= qi);
-                        if (!live) pr = 0.0f;
-                    }
+                    const float pr = fast_exp2(s[qb][r]);     // exp2(-inf) = 0
                     float z = 1.0f;
                     if (DROPOUT) {
                         const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)qi,
@@ -254,10 +282,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_operand<CH>(doL, 16 * qc, 32 * db, lane), bp, dva[db], 0, 0, 0);
-                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_operand<CH>(qL, 16 * qc, 32 * db, lane), bs, dka[db], 0, 0, 0);
+                    const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
+                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(doL, o0, o1), bp,
+                                                                     dva[db], 0, 0, 0);
+                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qL, o0, o1), bs,
+                                                                     dka[db], 0, 0, 0);
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
@@ -272,7 +301,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                 }
         }
         __syncthreads();
-        if (i0 + BQ < N) issue_tile(i0 + BQ);     // Q/dO/LSE/D are not read again this tile
+        if (i0 > i_first) issue_tile(i0 - BQ);    // Q/dO/LSE/D are not read again this tile
 
         // dQ_tile = dS K over the block's 128 keys, 32x32 blocks dealt to the waves
 #pragma unroll
@@ -284,8 +313,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
             for (int kc = 0; kc < kBKV / 16; ++kc)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    tr_operand<BQ / 8>(dsL, 16 * kc, 32 * qb, lane),
-                    tr_operand<CH>(kL, 16 * kc, 32 * db, lane), acc, 0, 0, 0);
+                    tr_read(dsL, tsoff[qb][0] + 16 * kc * SROW, tsoff[qb][1] + 16 * kc * SROW),
+                    tr_read(kL, troff[db][0] + 16 * kc * ROW, troff[db][1] + 16 * kc * ROW), acc,
+                    0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -315,10 +345,12 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     }
 }
 
-// D_i = <dO_i, O_i> in fp32 and a zeroed dQ accumulator; 8 lanes per row.
+// D_i = <dO_i, O_i> in fp32, LSE_i in log2 units, and a zeroed dQ
+// accumulator; 8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __bf16* dout,
-                                                      float* dsum, float* dq_acc, int rows) {
+                                                      const float* lse, float* dsum, float* lse2,
+                                                      float* dq_acc, int rows) {
     constexpr int PER = D / 8;     // elements per lane
     const int row = blockIdx.x * 32 + (threadIdx.x >> 3);
     const int part = threadIdx.x & 7;
@@ -338,7 +370,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __b
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
-    if (row < rows && part == 0) dsum[row] = acc;
+    if (row < rows && part == 0) {
+        dsum[row] = acc;
+        lse2[row] = lse[row] * kLog2e;
+    }
 }
 
 // dQ = bf16(dQ accumulator), 8 elements per thread.
@@ -363,7 +398,7 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
     p.k = (const __bf16*)a.k;
     p.v = (const __bf16*)a.v;
     p.dout = (const __bf16*)a.dout;
-    p.lse = a.lse;
+    p.lse2 = a.lse2;
     p.dsum = a.dsum;
     p.dq_acc = a.dq_accum;
     p.dk = (__bf16*)a.dk;
@@ -386,7 +421,8 @@ template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     const int rows = a.s.B * a.s.H * a.s.N;
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 31) / 32), dim3(256), 0, st,
-                       (const __bf16*)a.o, (const __bf16*)a.dout, a.dsum, a.dq_accum, rows);
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.dsum, a.lse2,
+                       a.dq_accum, rows);
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
     hipError_t e;
     if (a.s.causal)

@@ -38,6 +38,7 @@ struct BwdArgs {
     void* dv;
     float* dq_accum;   // workspace: fp32 [B,H,N,d]
     float* dsum;       // workspace: fp32 [B,H,N], D_i = <dO_i, O_i>
+    float* lse2;       // workspace: fp32 [B,H,N], LSE_i * log2(e)
 };
 
 // Dropout threshold: an element is dropped iff Philox word 0 < thr, thr = ceil(p * 2^32).

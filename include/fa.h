@@ -113,8 +113,9 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
 
 /*
  * Bytes of device scratch that fa_bwd / fa_bwd_f32 need: an fp32 [B,H,N,d]
- * dQ accumulator plus the fp32 [B,H,N] row terms D_i = <dO_i, O_i>, each
- * rounded up to 256 bytes. Returns 0 if an argument is out of range.
+ * dQ accumulator, the fp32 [B,H,N] row terms D_i = <dO_i, O_i>, and the
+ * fp32 [B,H,N] log-sum-exp in log2 units, each rounded up to 256 bytes.
+ * Returns 0 if an argument is out of range.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 

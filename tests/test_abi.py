@@ -44,7 +44,7 @@ def test_workspace_size(L):
     B, H, N, d = 2, 16, 4096, 64
     rows = B * H * N
     rnd = lambda x: (x + 255) // 256 * 256
-    assert L.fa_bwd_workspace_size(B, H, N, d) == rnd(rows * d * 4) + rnd(rows * 4)
+    assert L.fa_bwd_workspace_size(B, H, N, d) == rnd(rows * d * 4) + 2 * rnd(rows * 4)
     assert L.fa_bwd_workspace_size(0, 1, 1, 64) == 0
     assert L.fa_bwd_workspace_size(1024, 1024, 1024, 128) == 0   # above 2^31 - 1 elements
 
