@@ -21,9 +21,10 @@
 //   ds_read_b64_tr_b16, which transposes 4x16 blocks of V on the fly.
 // * K/V tiles travel HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //   staging), double-buffered, with out-of-range rows of a ragged tail
-//   returned as zeros by the buffer range check. Chunks of 16 bytes are
-//   XOR-swizzled per row (chunk_swizzle) so that both the K reads (16 rows,
-//   same columns) and the transposed V reads hit distinct LDS banks.
+//   returned as zeros by the buffer range check. LDS rows are padded (K by 16
+//   bytes, V by 64) so that both the K reads (16 rows, same columns) and the
+//   transposed V reads hit distinct LDS banks, and every operand read is one
+//   base register plus an immediate offset.
 // * The scale is applied in fp32 after the product and folded with log2(e)
 //   into the exp2 argument: p = exp2(s * c - m2) with c = scale * log2(e) and
 //   m2 the running maximum of s * c. The division by l (and by 1 - p_drop)
@@ -51,7 +52,7 @@ constexpr float RESCALE_SLACK = 8.0f;
 
 // LDS operand reads kept in flight ahead of the matrix-core product that uses them.
 #ifndef FA_FWD_PREFETCH
-#define FA_FWD_PREFETCH 2
+#define FA_FWD_PREFETCH 4
 #endif
 constexpr int kPrefetch = FA_FWD_PREFETCH;
 
@@ -68,6 +69,117 @@ struct FwdParamsB {
     PhiloxKey key;
 };
 
+// Workgroup -> (head, query block). When B*H is a multiple of 8 the heads are
+// split over the 8 XCDs (workgroup IDs are dealt round-robin over the XCDs),
+// so each head's K/V is read through one XCD's L2. An XCD takes its heads
+// kHeadGroup at a time; within a group the query blocks of all its heads run
+// longest-first (causal), which shortens the tail that the last group leaves.
+#ifndef FA_HEAD_GROUP
+#define FA_HEAD_GROUP 4
+#endif
+constexpr int kHeadGroup = FA_HEAD_GROUP;
+
+__device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool causal, int& bh, int& qb) {
+    if ((heads & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        const int hpx = heads >> 3;
+        const int g = hpx % kHeadGroup == 0 ? kHeadGroup : 1;
+        const int grp = slot / (g * nqb), in = slot - grp * (g * nqb);
+        bh = (grp * g + in % g) * 8 + xcd;
+        qb = in / g;
+    } else {
+        bh = bid % heads;
+        qb = bid / heads;
+    }
+    if (causal) qb = nqb - 1 - qb;
+}
+
+// K/V tiles in LDS use padded rows instead of a swizzle, so that every
+// operand read of a lane is one base register plus an immediate offset:
+//  * K rows are read 16 rows x 16 bytes per pass (row operands); a row stride
+//    of 2D + 16 bytes puts 16 consecutive rows on 16 distinct 16-byte bank
+//    groups.
+//  * V is read transposed, 4 rows x 64 bytes per pass; a row stride of 2D + 64
+//    bytes puts 4 consecutive rows on 4 distinct 64-byte bank groups.
+// The copy engine writes 64 x 16 contiguous bytes per wave instruction, so the
+// pad chunks are copied too, from an out-of-range offset (zeros, no memory
+// access).
+template <int D, int BC>
+struct PaddedTiles {
+    static constexpr int CH = D / 8;                 // 16-byte chunks of data per row
+    static constexpr int KCH = CH + 1, VCH = CH + 4;
+    static constexpr int KS = KCH * 16, VS = VCH * 16;
+    static constexpr int K_TILE = BC * KS, V_TILE = BC * VS;
+    static_assert(BC * KCH % 64 == 0 && BC * VCH % 64 == 0, "tiles are whole copy blocks");
+};
+
+// Copy of rows [t*BC, t*BC + BC) of one head into a padded tile with RCH
+// chunks per row; the NW waves of the workgroup share the 1 KB copy blocks.
+// The per-lane source offsets within a tile are computed once; a tile adds
+// t * BC rows. Pad chunks read from far past the head (zeros, no memory
+// access; should the sum wrap for a huge head they load real bytes, which is
+// harmless: pad chunks are never read).
+template <int D, int BC, int RCH, int NW>
+struct TileCopy {
+    static constexpr int CH = D / 8, BLKS = BC * RCH / 64, PER = (BLKS + NW - 1) / NW;
+    static constexpr uint32_t kPad = 0xf0000000u;
+    uint32_t off[PER];
+
+    __device__ __forceinline__ TileCopy(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pos = (i * NW + wave) * 64 + lane;
+            const int row = pos / RCH, ch = pos % RCH;
+            off[i] = ch < CH ? (uint32_t)(row * D + ch * 8) * 2 : kPad;
+        }
+    }
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, FA_LDS char* base, int t, int wave) const {
+        // Tile offset as an opaque scalar: otherwise loop strength reduction
+        // turns every off[i] into a vector induction variable of its own.
+        const uint32_t toff = __builtin_amdgcn_readfirstlane((uint32_t)t * (BC * D * 2));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int blk = i * NW + wave;
+            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), off[i] + toff);
+        }
+    }
+};
+
+// Per-lane base offsets of the operand reads in padded tiles.
+//  K operand (S^T = K Q^T, A side): key row l32 (+32 per key block), d = 16c + 8hi .. +7.
+//  V^T operand (O^T = V^T P^T, A side): d = 32db + column, keys 16c + 4(lane/32) + {0..3}
+//  and +8; within a 16-lane group, lane s reads key row s/4 and 4 columns at 4(s%4).
+template <int D, int BC>
+__device__ __forceinline__ int k_base(int lane) {
+    return (lane & 31) * PaddedTiles<D, BC>::KS + (lane >> 5) * 16;
+}
+template <int D, int BC>
+__device__ __forceinline__ int v_base(int lane) {
+    return (4 * (lane >> 5) + ((lane & 15) >> 2)) * PaddedTiles<D, BC>::VS +
+           2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+}
+// K operand i = c * KB + kb of a tile (KB = BC / 32 key blocks).
+template <int D, int BC>
+__device__ __forceinline__ bf16x8 k_operand(const FA_LDS char* kt, int kbase, int i) {
+    constexpr int KB = BC / 32;
+    return *(const FA_LDS bf16x8*)(kt + kbase + (i / KB) * 32 + (i % KB) * 32 * PaddedTiles<D, BC>::KS);
+}
+// V^T operand j = c * DB + db of a tile (DB = D / 32 d blocks, c = 16-key chunk).
+template <int D, int BC>
+__device__ __forceinline__ bf16x8 v_operand(const FA_LDS char* vt, int vbase, int j) {
+    constexpr int DB = D / 32, VS = PaddedTiles<D, BC>::VS;
+    bf16x8 a;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS s16x4*)(vt + vbase + (16 * (j / DB) + 8 * half) * VS + 64 * (j % DB)));
+        const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * half + e] = xb[e];
+    }
+    return a;
+}
+
 template <int D, int BC, int NW, int RB, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
 void fwd_bf16_kernel(FwdParamsB p) {
@@ -78,32 +190,22 @@ void fwd_bf16_kernel(FwdParamsB p) {
     constexpr int KB = BC / 32;            // 32-key blocks per tile
     constexpr int NC = BC / 16;            // 16-key chunks per tile (PV k-steps)
     constexpr int DB = D / 32;             // 32-wide d blocks of O^T
-    constexpr int TILE_BYTES = BC * D * 2;
-    constexpr int LOADS = BC * CH / (64 * NW);   // 16-byte loads per lane per tensor per tile
-    static_assert(LOADS * 64 * NW == BC * CH, "tile must split evenly over the waves");
+    using PT = PaddedTiles<D, BC>;
+    constexpr int K_TILE = PT::K_TILE, V_TILE = PT::V_TILE;
     constexpr int S_MFMA = KB * (D / 16);  // K operands of one score tile
     constexpr int PV_MFMA = NC * DB;       // V^T operands of one PV update
 
-    __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];   // two K tiles
-    __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];   // two V tiles
+    __shared__ __attribute__((aligned(1024))) char kbuf[2 * K_TILE];   // two K tiles
+    __shared__ __attribute__((aligned(1024))) char vbuf[2 * V_TILE];   // two V tiles
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
     // ---- workgroup -> (head, query block)
     int bh, qb;
-    const int bid = blockIdx.x;
-    if ((p.heads & 7) == 0) {
-        const int xcd = bid & 7, slot = bid >> 3;
-        bh = (slot / p.nqb) * 8 + xcd;
-        qb = slot % p.nqb;
-    } else {
-        bh = bid % p.heads;
-        qb = bid / p.heads;
-    }
-    if (CAUSAL) qb = p.nqb - 1 - qb;
+    decode_block(blockIdx.x, p.heads, p.nqb, CAUSAL, bh, qb);
     const int b = bh / p.H, h = bh - b * p.H;
     const int N = p.N;
     const size_t head = (size_t)bh * N * D;
@@ -151,55 +253,14 @@ void fwd_bf16_kernel(FwdParamsB p) {
     // Tiles this wave needs: causal rows stop at their diagonal; rows past N need none.
     const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + WR - 1, N - 1) / BC + 1) : ntiles;
 
-    // HBM -> LDS copy of rows [t*BC, t*BC + BC) of K and V, chunks swizzled per row.
+    // HBM -> LDS copy of K and V tile t into buffer buf.
+    const TileCopy<D, BC, PT::KCH, NW> kcopy(wave, lane);
+    const TileCopy<D, BC, PT::VCH, NW> vcopy(wave, lane);
     auto issue = [&](int t, int buf) {
-        const int k0 = t * BC;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int blk = i * NW + wave;             // 1 KB block of the tile written by this wave
-            const int pos = blk * 64 + lane;           // 16-byte slot in the tile
-            const int row = pos / CH, sw = pos % CH;
-            const uint32_t off = ((uint32_t)(k0 + row) * D + (uint32_t)((sw ^ chunk_swizzle<CH>(row)) * 8)) * 2;
-            buffer_to_lds16(rs_k, (FA_LDS void*)((FA_LDS char*)kbuf + buf * TILE_BYTES + blk * 1024), off);
-            buffer_to_lds16(rs_v, (FA_LDS void*)((FA_LDS char*)vbuf + buf * TILE_BYTES + blk * 1024), off);
-        }
+        kcopy.issue(rs_k, (FA_LDS char*)kbuf + buf * K_TILE, t, wave);
+        vcopy.issue(rs_v, (FA_LDS char*)vbuf + buf * V_TILE, t, wave);
     };
-
-    // Per-lane LDS byte offsets of the operand reads. The K operand i = c*KB + kb
-    // is key row 32kb + l32, d = 16c + 8hi .. +7: koff[c] plus kb*32 rows. The
-    // V^T operand j = c*DB + db holds d = 32db + l32 and keys 16c + 4hi + {0..3}
-    // (first read) and 16c + 8 + 4hi + {0..3} (second read): voff[db][half]
-    // plus 16c rows. Within a 16-lane group, lane s of the transposed read
-    // addresses key (s / 4) and columns 4 (s % 4) .. +3 of its 4x16 block. The
-    // swizzle depends only on the low row bits, so row-block terms are immediates.
-    int koff[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) koff[c] = tile_offset<CH>(l32, 16 * c + 8 * hi);
-    int voff[DB][2];
-    {
-        const int grp = lane >> 4, sl = lane & 15;
-        const int vd = 16 * (grp & 1) + 4 * (sl & 3);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                voff[db][half] = tile_offset<CH>(8 * half + 4 * (grp >> 1) + (sl >> 2), 32 * db + vd);
-    }
-    auto k_operand = [&](const FA_LDS char* kt, int i) {
-        return *(const FA_LDS bf16x8*)(kt + koff[i / KB] + (i % KB) * 32 * ROW_BYTES);
-    };
-    auto v_operand = [&](const FA_LDS char* vt, int j) {
-        bf16x8 a;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (FA_LDS s16x4*)(vt + voff[j % DB][half] + 16 * (j / DB) * ROW_BYTES));
-            const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[4 * half + e] = xb[e];
-        }
-        return a;
-    };
+    const int kbase = k_base<D, BC>(lane), vbase = v_base<D, BC>(lane);
 
     issue(0, 0);
 
@@ -210,18 +271,21 @@ void fwd_bf16_kernel(FwdParamsB p) {
         if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
         if (t >= ntiles_w) continue;               // whole tile above this wave's diagonal
 
-        const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * TILE_BYTES;
-        const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * TILE_BYTES;
+        const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * K_TILE;
+        const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * V_TILE;
         const int k0 = t * BC;
 
         // ---- S^T = K Q^T. Element (kb, r) of a lane in row block rb: key row
         // 32kb + 8(r/4) + 4hi + r%4 of the tile against query row qw + 32rb + l32.
         // Each K operand read feeds the RB row blocks.
+        // The scheduling fences keep kPrefetch operand reads in flight; without
+        // them the compiler sinks each read to just before its product.
         f32x16 s[RB][KB];
         {
             bf16x8 kop[kPrefetch];
 #pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand(kt, j);
+            for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC>(kt, kbase, j);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < S_MFMA; ++i) {
                 const int kb = i % KB, c = i / KB;
@@ -229,7 +293,8 @@ void fwd_bf16_kernel(FwdParamsB p) {
                 for (int rb = 0; rb < RB; ++rb)
                     s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[rb][c],
                                                                         c == 0 ? f32x16{} : s[rb][kb], 0, 0, 0);
-                if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand(kt, i + kPrefetch);
+                if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC>(kt, kbase, i + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
@@ -240,14 +305,14 @@ void fwd_bf16_kernel(FwdParamsB p) {
             const int my_q = row0 + l32;
             // ---- mask: only tiles that cross the diagonal or the ragged end
             if ((CAUSAL && k0 + BC - 1 > row0) || (k0 + BC > N)) {
-                const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
+                // last visible key, relative to the lane's first key of the tile;
+                // element offsets are then compile-time constants
+                const int rel = (CAUSAL ? min(my_q, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        s[rb][kb][r] = key > lim ? -INFINITY : s[rb][kb][r];
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        s[rb][kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[rb][kb][r];
             }
 
             // ---- online softmax (log2 domain)
@@ -309,14 +374,16 @@ void fwd_bf16_kernel(FwdParamsB p) {
         {
             bf16x8 vop[kPrefetch];
 #pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand(vt, j);
+            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC>(vt, vbase, j);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < PV_MFMA; ++j) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     oacc[rb][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[rb][j / DB],
                                                                                oacc[rb][j % DB], 0, 0, 0);
-                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand(vt, j + kPrefetch);
+                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC>(vt, vbase, j + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
