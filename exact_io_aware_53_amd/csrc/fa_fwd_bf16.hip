@@ -69,17 +69,17 @@ struct FwdParamsB {
     PhiloxKey key;
 };
 
-// Workgroup -> (head, query block). When B*H is a multiple of 8 the heads are
+// Workgroup -> (head, block index). When B*H is a multiple of 8 the heads are
 // split over the 8 XCDs (workgroup IDs are dealt round-robin over the XCDs),
 // so each head's K/V is read through one XCD's L2. An XCD takes its heads
-// kHeadGroup at a time; within a group the query blocks of all its heads run
-// longest-first (causal), which shortens the tail that the last group leaves.
+// kHeadGroup at a time, the blocks of a group interleaved over its heads;
+// `reverse` deals the blocks last-first.
 #ifndef FA_HEAD_GROUP
-#define FA_HEAD_GROUP 4
+#define FA_HEAD_GROUP 2
 #endif
 constexpr int kHeadGroup = FA_HEAD_GROUP;
 
-__device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool causal, int& bh, int& qb) {
+__device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool reverse, int& bh, int& qb) {
     if ((heads & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
         const int hpx = heads >> 3;
@@ -91,7 +91,7 @@ __device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool c
         bh = bid % heads;
         qb = bid / heads;
     }
-    if (causal) qb = nqb - 1 - qb;
+    if (reverse) qb = nqb - 1 - qb;
 }
 
 // K/V tiles in LDS use padded rows instead of a swizzle, so that every
@@ -203,9 +203,12 @@ void fwd_bf16_kernel(FwdParamsB p) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // ---- workgroup -> (head, query block)
-    int bh, qb;
-    decode_block(blockIdx.x, p.heads, p.nqb, CAUSAL, bh, qb);
+    // ---- workgroup -> (head, query blocks). Causal: a workgroup takes the
+    // query blocks nqb-1-k and k of its head, one after the other, so every
+    // workgroup has the same number of key tiles (nqb + 1 when nqb is even)
+    // and no long block is left to run alone at the end of the grid.
+    int bh, slot;
+    decode_block(blockIdx.x, p.heads, CAUSAL ? (p.nqb + 1) / 2 : p.nqb, false, bh, slot);
     const int b = bh / p.H, h = bh - b * p.H;
     const int N = p.N;
     const size_t head = (size_t)bh * N * D;
@@ -214,209 +217,223 @@ void fwd_bf16_kernel(FwdParamsB p) {
     const auto rs_k = make_rsrc(p.k + head, head_bytes);
     const auto rs_v = make_rsrc(p.v + head, head_bytes);
 
-    const int q0 = qb * BR;
-    const int qw = q0 + wave * WR;         // first query row of this wave
-    // Row block rb of this wave holds query rows qw + 32rb .. +31; lane's row: qw + 32rb + l32.
-
-    // ---- Q rows as B operands: chunk c holds d = 16c + 8*hi .. +7
-    bf16x8 qreg[RB][D / 16];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            qreg[rb][c] = __builtin_bit_cast(
-                bf16x8, buffer_load16(rs_q, (uint32_t)((qw + 32 * rb + l32) * D + 16 * c + 8 * hi) * 2));
-
-    f32x16 oacc[RB][DB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][i][r] = 0.0f;
-    float m2[RB], lsum[RB], lbf[RB];   // reference max of s*c; shares of sum P~ (fp32) and sum bf16(P~)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m2[rb] = -INFINITY;
-        lsum[rb] = 0.0f;
-        lbf[rb] = 0.0f;
-    }
-
-    // Dropout generator state of each row block's row (counter b, h, row, key).
-    PhiloxRow philox[RB] = {PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + l32), p.key)};
-#pragma unroll
-    for (int rb = 1; rb < RB; ++rb)
-        philox[rb] = PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + 32 * rb + l32), p.key);
-
-    const int last_q = min(N, q0 + BR) - 1;
-    const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
-    // Tiles this wave needs: causal rows stop at their diagonal; rows past N need none.
-    const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + WR - 1, N - 1) / BC + 1) : ntiles;
-
-    // HBM -> LDS copy of K and V tile t into buffer buf.
     const TileCopy<D, BC, PT::KCH, NW> kcopy(wave, lane);
     const TileCopy<D, BC, PT::VCH, NW> vcopy(wave, lane);
-    auto issue = [&](int t, int buf) {
-        kcopy.issue(rs_k, (FA_LDS char*)kbuf + buf * K_TILE, t, wave);
-        vcopy.issue(rs_v, (FA_LDS char*)vbuf + buf * V_TILE, t, wave);
-    };
     const int kbase = k_base<D, BC>(lane), vbase = v_base<D, BC>(lane);
 
-    issue(0, 0);
+    auto run_block = [&](int qb) {
+        const int q0 = qb * BR;
+        const int qw = q0 + wave * WR;         // first query row of this wave
+        // Row block rb of this wave holds query rows qw + 32rb .. +31; lane's row: qw + 32rb + l32.
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
-        if (t >= ntiles_w) continue;               // whole tile above this wave's diagonal
-
-        const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * K_TILE;
-        const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * V_TILE;
-        const int k0 = t * BC;
-
-        // ---- S^T = K Q^T. Element (kb, r) of a lane in row block rb: key row
-        // 32kb + 8(r/4) + 4hi + r%4 of the tile against query row qw + 32rb + l32.
-        // Each K operand read feeds the RB row blocks.
-        // The scheduling fences keep kPrefetch operand reads in flight; without
-        // them the compiler sinks each read to just before its product.
-        f32x16 s[RB][KB];
-        {
-            bf16x8 kop[kPrefetch];
+        // ---- Q rows as B operands: chunk c holds d = 16c + 8*hi .. +7
+        bf16x8 qreg[RB][D / 16];
 #pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC>(kt, kbase, j);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int i = 0; i < S_MFMA; ++i) {
-                const int kb = i % KB, c = i / KB;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[rb][c],
-                                                                        c == 0 ? f32x16{} : s[rb][kb], 0, 0, 0);
-                if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC>(kt, kbase, i + kPrefetch);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+            for (int c = 0; c < D / 16; ++c)
+                qreg[rb][c] = __builtin_bit_cast(
+                    bf16x8, buffer_load16(rs_q, (uint32_t)((qw + 32 * rb + l32) * D + 16 * c + 8 * hi) * 2));
 
-        bf16x8 pb[RB][NC];
+        f32x16 oacc[RB][DB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[rb][i][r] = 0.0f;
+        float m2[RB], lsum[RB], lbf[RB];   // reference max of s*c; shares of sum P~ (fp32) and sum bf16(P~)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int row0 = qw + 32 * rb;     // first row of the block
-            const int my_q = row0 + l32;
-            // ---- mask: only tiles that cross the diagonal or the ragged end
-            if ((CAUSAL && k0 + BC - 1 > row0) || (k0 + BC > N)) {
-                // last visible key, relative to the lane's first key of the tile;
-                // element offsets are then compile-time constants
-                const int rel = (CAUSAL ? min(my_q, N - 1) : N - 1) - k0 - 4 * hi;
+            m2[rb] = -INFINITY;
+            lsum[rb] = 0.0f;
+            lbf[rb] = 0.0f;
+        }
+
+        // Dropout generator state of each row block's row (counter b, h, row, key).
+        PhiloxRow philox[RB] = {PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + l32), p.key)};
+#pragma unroll
+        for (int rb = 1; rb < RB; ++rb)
+            philox[rb] = PhiloxRow((uint32_t)b, (uint32_t)h, (uint32_t)(qw + 32 * rb + l32), p.key);
+
+        const int last_q = min(N, q0 + BR) - 1;
+        const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
+        // Tiles this wave needs: causal rows stop at their diagonal; rows past N need none.
+        const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + WR - 1, N - 1) / BC + 1) : ntiles;
+
+        // HBM -> LDS copy of K and V tile t into buffer buf.
+        auto issue = [&](int t, int buf) {
+            kcopy.issue(rs_k, (FA_LDS char*)kbuf + buf * K_TILE, t, wave);
+            vcopy.issue(rs_v, (FA_LDS char*)vbuf + buf * V_TILE, t, wave);
+        };
+        issue(0, 0);
+
+        for (int t = 0; t < ntiles; ++t) {
+            const int buf = t & 1;
+            wait_vmem();
+            __syncthreads();
+            if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+            if (t >= ntiles_w) continue;               // whole tile above this wave's diagonal
+
+            const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * K_TILE;
+            const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * V_TILE;
+            const int k0 = t * BC;
+
+            // ---- S^T = K Q^T. Element (kb, r) of a lane in row block rb: key row
+            // 32kb + 8(r/4) + 4hi + r%4 of the tile against query row qw + 32rb + l32.
+            // Each K operand read feeds the RB row blocks.
+            // The scheduling fences keep kPrefetch operand reads in flight; without
+            // them the compiler sinks each read to just before its product.
+            f32x16 s[RB][KB];
+            {
+                bf16x8 kop[kPrefetch];
+#pragma unroll
+                for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC>(kt, kbase, j);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < S_MFMA; ++i) {
+                    const int kb = i % KB, c = i / KB;
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[rb][c],
+                                                                            c == 0 ? f32x16{} : s[rb][kb], 0, 0, 0);
+                    if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC>(kt, kbase, i + kPrefetch);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            bf16x8 pb[RB][NC];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row0 = qw + 32 * rb;     // first row of the block
+                const int my_q = row0 + l32;
+                // ---- mask: only tiles that cross the diagonal or the ragged end
+                if ((CAUSAL && k0 + BC - 1 > row0) || (k0 + BC > N)) {
+                    // last visible key, relative to the lane's first key of the tile;
+                    // element offsets are then compile-time constants
+                    const int rel = (CAUSAL ? min(my_q, N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            s[rb][kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[rb][kb][r];
+                }
+
+                // ---- online softmax (log2 domain)
+                float mx = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[rb][kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[rb][kb][r];
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+                mx = max_with_partner32(mx) * p.sl2;
+                if (__builtin_amdgcn_ballot_w64(mx > m2[rb] + RESCALE_SLACK)) {
+                    const float m_new = fmaxf(m2[rb], mx);
+                    const float alpha = fast_exp2(m2[rb] - m_new);   // exp2(-inf) = 0 on the first tile
+                    lsum[rb] *= alpha;
+                    lbf[rb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+                    m2[rb] = m_new;
+                }
+                uint32_t keep[KB];
+                if (DROPOUT) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        uint32_t bits = 0;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            bits |= (uint32_t)(philox[rb].word0((uint32_t)key) >= p.thr) << r;
+                        }
+                        keep[kb] = bits;
+                    }
+                }
+                const float neg = -m2[rb];
+                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const float x0 = fast_exp2(fmaf(s[rb][kb][r], p.sl2, neg));
+                        const float x1 = fast_exp2(fmaf(s[rb][kb][r + 1], p.sl2, neg));
+                        lsum[rb] += x0;
+                        lsum[rb] += x1;
+                        bf16x2 w;
+                        w[0] = (__bf16)x0;
+                        w[1] = (__bf16)x1;
+                        lbf[rb] = __builtin_amdgcn_fdot2_f32_bf16(w, ones, lbf[rb], false);
+                        if (DROPOUT) {
+                            w[0] = (__bf16)((keep[kb] >> r) & 1u ? x0 : 0.0f);
+                            w[1] = (__bf16)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
+                        }
+                        const int pc = kb * 2 + r / 8, pi = r % 8;
+                        pb[rb][pc][pi] = w[0];
+                        pb[rb][pc][pi + 1] = w[1];
+                    }
             }
 
-            // ---- online softmax (log2 domain)
-            float mx = -INFINITY;
+            // ---- O~^T += V^T P^T; each V^T operand read feeds the RB row blocks
+            {
+                bf16x8 vop[kPrefetch];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC>(vt, vbase, j);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
-            mx = max_with_partner32(mx) * p.sl2;
-            if (__builtin_amdgcn_ballot_w64(mx > m2[rb] + RESCALE_SLACK)) {
-                const float m_new = fmaxf(m2[rb], mx);
-                const float alpha = fast_exp2(m2[rb] - m_new);   // exp2(-inf) = 0 on the first tile
-                lsum[rb] *= alpha;
-                lbf[rb] *= alpha;
+                for (int j = 0; j < PV_MFMA; ++j) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        oacc[rb][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[rb][j / DB],
+                                                                                   oacc[rb][j % DB], 0, 0, 0);
+                    if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC>(vt, vbase, j + kPrefetch);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+
+        // ---- epilogue: O = O~ / (lb (1 - p)), LSE = (m2 + log2 l) ln 2
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int my_q = qw + 32 * rb + l32;
+            const float ltot = add_with_partner32(lsum[rb]);
+            const float lbtot = add_with_partner32(lbf[rb]);
+            const float inv = p.inv_keep / lbtot;
+            if (my_q < N) {
+                __bf16* orow = p.o + head + (size_t)my_q * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-                m2[rb] = m_new;
-            }
-            uint32_t keep[KB];
-            if (DROPOUT) {
+                    for (int g = 0; g < 4; ++g) {
+                        bf16x4 w;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    uint32_t bits = 0;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        bits |= (uint32_t)(philox[rb].word0((uint32_t)key) >= p.thr) << r;
+                        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(oacc[rb][db][4 * g + i] * inv);
+                        *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
                     }
-                    keep[kb] = bits;
-                }
-            }
-            const float neg = -m2[rb];
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float x0 = fast_exp2(fmaf(s[rb][kb][r], p.sl2, neg));
-                    const float x1 = fast_exp2(fmaf(s[rb][kb][r + 1], p.sl2, neg));
-                    lsum[rb] += x0;
-                    lsum[rb] += x1;
-                    bf16x2 w;
-                    w[0] = (__bf16)x0;
-                    w[1] = (__bf16)x1;
-                    lbf[rb] = __builtin_amdgcn_fdot2_f32_bf16(w, ones, lbf[rb], false);
-                    if (DROPOUT) {
-                        w[0] = (__bf16)((keep[kb] >> r) & 1u ? x0 : 0.0f);
-                        w[1] = (__bf16)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
-                    }
-                    const int pc = kb * 2 + r / 8, pi = r % 8;
-                    pb[rb][pc][pi] = w[0];
-                    pb[rb][pc][pi + 1] = w[1];
-                }
-        }
-
-        // ---- O~^T += V^T P^T; each V^T operand read feeds the RB row blocks
-        {
-            bf16x8 vop[kPrefetch];
-#pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC>(vt, vbase, j);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < PV_MFMA; ++j) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    oacc[rb][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[rb][j / DB],
-                                                                               oacc[rb][j % DB], 0, 0, 0);
-                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC>(vt, vbase, j + kPrefetch);
-                __builtin_amdgcn_sched_barrier(0);
+                if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m2[rb] + fast_log2(ltot)) * kLn2;
             }
         }
-    }
+    };
 
-    // ---- epilogue: O = O~ / (lb (1 - p)), LSE = (m2 + log2 l) ln 2
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int my_q = qw + 32 * rb + l32;
-        const float ltot = add_with_partner32(lsum[rb]);
-        const float lbtot = add_with_partner32(lbf[rb]);
-        const float inv = p.inv_keep / lbtot;
-        if (my_q < N) {
-            __bf16* orow = p.o + head + (size_t)my_q * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = (__bf16)(oacc[rb][db][4 * g + i] * inv);
-                    *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
-                }
-            if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m2[rb] + fast_log2(ltot)) * kLn2;
+    if (CAUSAL) {
+        const int longer = p.nqb - 1 - slot;
+        run_block(longer);
+        if (slot != longer) {
+            __syncthreads();     // every wave is done with the buffers the next block refills
+            run_block(slot);
         }
+    } else {
+        run_block(slot);
     }
 }
 
-// Keys per K/V tile and waves (32 query rows each) per workgroup, by head size.
+// Keys per K/V tile and waves (32 query rows each) per workgroup: 128-key tiles
+// and 8 waves, one workgroup per CU (two waves per SIMD) sharing each K/V copy.
 #ifndef FA_FWD_BC
-#define FA_FWD_BC 64
+#define FA_FWD_BC 128
 #endif
 #ifndef FA_FWD_NW
-#define FA_FWD_NW 4
+#define FA_FWD_NW 8
 #endif
 // 32-row query blocks per wave: each K/V operand read from LDS feeds this many products.
 #ifndef FA_FWD_RB
@@ -440,7 +457,8 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
     p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * p.nqb),
+    const int blocks = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * blocks),
                        dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }

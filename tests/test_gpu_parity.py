@@ -89,8 +89,11 @@ def abs_err(g, ref):
     return float(np.abs(g - ref).max())
 
 
+# The last two shapes have B*H = 8 and 32: workgroups are then dealt to XCDs by
+# head, one head at a time and four heads at a time respectively.
 SMALL = [(1, 2, 1, 64), (1, 2, 17, 64), (2, 1, 127, 128), (1, 1, 128, 64), (1, 2, 129, 128),
-         (1, 1, 1000, 64), (2, 2, 300, 128), (1, 1, 64, 128), (3, 1, 257, 64)]
+         (1, 1, 1000, 64), (2, 2, 300, 128), (1, 1, 64, 128), (3, 1, 257, 64),
+         (1, 8, 300, 64), (2, 16, 520, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
