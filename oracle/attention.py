@@ -18,7 +18,11 @@ The Solution", last paragraph). So the oracle is that plain definition:
 * scores S_ij = s * <Q_i, K_j> with s = 1/sqrt(d) (DL0056, "Mathematical
   Formulation": the scaled score between query row i and key row j);
 * causal masking: query i sees keys j <= i only (inferensys, paragraph on
-  causal masking); a masked score takes no part in the softmax;
+  causal masking); a masked score takes no part in the softmax. When the
+  query rows are the last Nq positions of a longer key sequence (new tokens
+  against the key/value cache that inference servers keep; inferensys,
+  paragraph on integration with inference servers), query i sits at key
+  position key_offset + i and sees keys j <= key_offset + i;
 * row softmax P = softmax(S) and O = P V (emergent.sh, section "Why Regular
   Attention Becomes a Bottleneck": scores, softmax weights, weighted values);
 * the per-row statistic that the method keeps for the backward pass is the
@@ -58,30 +62,35 @@ def _dropout_p(dropout_p) -> float:
     return p
 
 
-def scores(q, k, scale: float, causal: bool, rows=None) -> np.ndarray:
-    """Scaled scores of the given query rows against every key, masked entries = -inf."""
+def scores(q, k, scale: float, causal: bool, rows=None, key_offset: int = 0) -> np.ndarray:
+    """Scaled scores of the given query rows against every key, masked entries = -inf.
+
+    Causal: query row i sees keys j <= key_offset + i.
+    """
     q, k = _f64(q), _f64(k)
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q[rows] @ k.T)
     if causal:
-        s[np.arange(n)[None, :] > rows[:, None]] = -np.inf
+        s[np.arange(n)[None, :] > rows[:, None] + int(key_offset)] = -np.inf
     return s
 
 
 def forward(q, k, v, scale: float, causal: bool = False, dropout_p=0.0, seed: int = 0,
-            b: int = 0, h: int = 0, rows=None):
+            b: int = 0, h: int = 0, rows=None, key_offset: int = 0):
     """Attention output and log-sum-exp for one head (b, h).
 
-    q, k, v: [N, d] arrays (any real dtype; widened exactly to fp64).
-    rows: query rows to evaluate (default: all N).
+    q: [Nq, d], k, v: [Nk, d] arrays (any real dtype; widened exactly to fp64).
+    rows: query rows to evaluate (default: all Nq).
+    key_offset: key position of query row 0 for the causal mask (0 when the
+    queries and keys are the same sequence; Nk - Nq for the last Nq positions).
     Returns (O [len(rows), d], LSE [len(rows)]), both fp64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     p = _dropout_p(dropout_p)
-    s = scores(q, k, scale, causal, rows)
+    s = scores(q, k, scale, causal, rows, key_offset)
     m = s.max(axis=1)
     with np.errstate(under="ignore"):
         lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))

@@ -26,13 +26,14 @@ def randn(shape, seed, scale=1.0):
 
 
 # ---------------------------------------------------------------- brute force
-def brute_forward(q, k, v, scale, causal, keep=None, p=0.0):
-    """Scalar loops with math.fsum; keep[i][j] is the dropout keep mask."""
+def brute_forward(q, k, v, scale, causal, keep=None, p=0.0, key_offset=0):
+    """Scalar loops with math.fsum; keep[i][j] is the dropout keep mask; causal query i
+    sits at key position key_offset + i."""
     q, k, v = q.tolist(), k.tolist(), v.tolist()
     n, d = len(k), len(k[0])
     outs, lses = [], []
     for i in range(len(q)):
-        js = [j for j in range(n) if (not causal or j <= i)]
+        js = [j for j in range(n) if (not causal or j <= key_offset + i)]
         s = [scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in js]
         m = max(s)
         l = math.fsum(math.exp(x - m) for x in s)
@@ -157,6 +158,49 @@ def test_forward_matches_bruteforce():
 
 def test_forward_matches_torch_sdpa_float64():
     assert pin_sdpa(A.forward) <= 1e-12
+
+
+def _maxdiff(a, b):
+    """Largest absolute difference; a NaN anywhere counts as an infinite error."""
+    d = np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))
+    return float("inf") if np.isnan(d).any() else float(d.max())
+
+
+def pin_key_offset(fwd):
+    """Query blocks placed at an offset in a longer key sequence (decode shape):
+    brute force, torch SDPA on the visible keys of each row, and agreement with the
+    same-sequence causal rows that the offset stands for."""
+    err = 0.0
+    for (nq, nk, d, causal, seed) in [(1, 9, 4, True, 40), (3, 11, 2, True, 41), (4, 4, 3, True, 42),
+                                      (2, 7, 4, False, 43), (5, 12, 3, True, 44)]:
+        q, k, v = randn((nq, d), seed, 2.0), randn((nk, d), seed + 1), randn((nk, d), seed + 2)
+        s = 1 / math.sqrt(d)
+        off = nk - nq
+        o, l = fwd(q, k, v, s, causal, key_offset=off)
+        o_ref, l_ref = brute_forward(q, k, v, s, causal, key_offset=off)
+        err = max(err, _maxdiff(o, o_ref), _maxdiff(l, l_ref))
+        for i in range(nq):
+            vis = off + i + 1 if causal else nk
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[i:i + 1])[None], torch.from_numpy(k[:vis])[None],
+                torch.from_numpy(v[:vis])[None], scale=s)[0].numpy()
+            err = max(err, _maxdiff(o[i], ref[0]))
+        # the last nq rows of a same-sequence problem
+        qa = np.concatenate([randn((off, d), seed + 3), q]) if off else q
+        o_rows, l_rows = fwd(qa, k, v, s, causal, rows=np.arange(off, nk))
+        err = max(err, _maxdiff(o, o_rows), _maxdiff(l, l_rows))
+    return err
+
+
+def test_forward_key_offset():
+    assert pin_key_offset(A.forward) <= 1e-12
+
+
+def test_single_query_at_end_sees_every_key():
+    q, k, v = randn((1, 8), 50, 2.0), randn((37, 8), 51), randn((37, 8), 52)
+    o_c, l_c = A.forward(q, k, v, 0.3, True, key_offset=36)
+    o_n, l_n = A.forward(q, k, v, 0.3, False)
+    assert np.array_equal(o_c, o_n) and np.array_equal(l_c, l_n)
 
 
 def test_forward_closed_forms():
@@ -335,15 +379,17 @@ def test_keep_fraction_one_head():
 
 # ------------------------------------------------- planted mistakes fail a pin
 def _mutant_forward(kind):
-    def fwd(q, k, v, scale, causal=False, dropout_p=0.0, seed=0, b=0, h=0, rows=None):
+    def fwd(q, k, v, scale, causal=False, dropout_p=0.0, seed=0, b=0, h=0, rows=None, key_offset=0):
         q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
         n = k.shape[0]
-        rows_ = np.arange(q.shape[0])
+        rows_ = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        q = q[rows_]
         sc = 1.0 if kind == "no_scale" else scale
         s = sc * (q @ k.T)
+        off = {"offset_ignored": 0, "offset_negated": -key_offset}.get(kind, key_offset)
         if causal:
-            bad = (np.arange(n)[None, :] < rows_[:, None]) if kind == "anti_causal" else \
-                  (np.arange(n)[None, :] > rows_[:, None])
+            bad = (np.arange(n)[None, :] < rows_[:, None] + off) if kind == "anti_causal" else \
+                  (np.arange(n)[None, :] > rows_[:, None] + off)
             s[bad] = -np.inf
         m = s.max(axis=1)
         l = np.exp(s - m[:, None]).sum(axis=1)
@@ -388,6 +434,11 @@ def test_planted_forward_mistakes_are_caught(kind):
 def test_planted_dropout_scaling_mistake_is_caught():
     fwd = _mutant_forward("dropout_unscaled")
     assert pin_bruteforce(fwd) > 1e-6
+
+
+@pytest.mark.parametrize("kind", ["offset_ignored", "offset_negated", "no_scale"])
+def test_planted_key_offset_mistakes_are_caught(kind):
+    assert pin_key_offset(_mutant_forward(kind)) > 1e-6, kind
 
 
 @pytest.mark.parametrize("kind", ["no_D", "dk_unscaled", "dv_transposed"])
