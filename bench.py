@@ -30,7 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "fwd_causal_q4_bf16_b2h32n8192d128"
 FWD_BWD_WORKLOAD = "fwdbwd_causal_dropout_bf16_b2h16n4096d64"
-FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp"]
+FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp",
+               "exact_io_aware_53_amd/csrc/fa_tiles.hpp"]
 
 
 def source_hash(paths):

@@ -8,6 +8,7 @@ CPU or PyTorch fallback: if libfa.so is missing, every call raises.
 
     o, lse = fwd(q, k, v, causal=True)             # q, k, v: [B, H, N, d] bf16 or fp32 on the GPU
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    o, lse = fwd_decode(q_new, k_cache, v_cache)   # [B, H, Nq, d] against [B, H, Nk, d], bf16
 """
 from __future__ import annotations
 
@@ -32,6 +33,8 @@ SIGNATURES = {
     "fa_bwd": (_I, _BWD_ARGS),
     "fa_bwd_f32": (_I, _BWD_ARGS),
     "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "fa_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "fa_fwd_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_dropout_mask": (_I, [_P, _I, _I, _I, _I, _I, _F, _U64, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -130,6 +133,35 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0,
     return dq, dk, dv
 
 
+def decode_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(lib().fa_fwd_decode_workspace_size(B, H, Nq, Nk, d))
+
+
+def fwd_decode(q, k, v, scale=None, causal=False, out=None, lse=None, workspace=None):
+    """Decode-shaped forward (bf16): q [B,H,Nq,d] against k, v [B,H,Nk,d], Nq <= Nk.
+    Returns (O [B,H,Nq,d] bf16, LSE [B,H,Nq] fp32)."""
+    B, H, Nq, d = _shape4(q, "q")
+    kshp = _shape4(k, "k")
+    if _shape4(v, "v") != kshp or kshp[:2] != (B, H) or kshp[3] != d:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H, d")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("fwd_decode takes bfloat16 tensors")
+    Nk = kshp[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_size(B, H, Nq, Nk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, H, Nq, Nk, d, scale, int(bool(causal)), ws_ptr, ws_bytes,
+                             _stream(q.device))
+    _check(st, "fa_fwd_decode")
+    return out, lse
+
+
 def dropout_mask(B, H, N, b, h, dropout_p, seed, device="cuda"):
     """[N, N] uint8 keep mask (1 = kept) of head (b, h), from the device generator."""
     mask = torch.empty((N, N), dtype=torch.uint8, device=device)
@@ -139,5 +171,5 @@ def dropout_mask(B, H, N, b, h, dropout_p, seed, device="cuda"):
     return mask
 
 
-__all__ = ["fwd", "bwd", "dropout_mask", "workspace_size", "lib", "FAError", "LIB_PATH",
-           "SIGNATURES"]
+__all__ = ["fwd", "bwd", "fwd_decode", "dropout_mask", "workspace_size", "decode_workspace_size", "lib",
+           "FAError", "LIB_PATH", "SIGNATURES"]

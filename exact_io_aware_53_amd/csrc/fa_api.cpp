@@ -24,7 +24,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_shape(int B, int H, int N, int d, float scale, float dropout_p) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;   // also rejects NaN
     if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;   // also rejects NaN
     if ((long long)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -39,6 +39,18 @@ size_t workspace_bytes(int B, int H, int N, int d) {
 }
 
 int map_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+bool decode_shape_ok(int B, int H, int Nq, int Nk, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || Nq > Nk) return false;
+    return (long long)B * H * Nk * d <= kMaxElems;
+}
+
+size_t decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk);
+    if (sp.S == 1) return 0;
+    const size_t rows = (size_t)B * H * sp.S * Nq;
+    return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
 
 fa::AttnShape shape(int B, int H, int N, int d, float scale, int causal, float p, uint64_t seed) {
     return fa::AttnShape{B, H, N, d, scale, causal != 0, p, seed};
@@ -112,6 +124,33 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                void* stream) {
     return bwd_common(false, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
                       dropout_p, seed, workspace, workspace_bytes_, stream);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  void* workspace, size_t workspace_bytes_, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const size_t need = decode_workspace_bytes(B, H, Nq, Nk, d);
+    if (need > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes_ < need)
+            return FA_ERR_INVALID_ARG;
+    }
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk);
+    const size_t rows = (size_t)B * H * sp.S * Nq;
+    float* o_part = need > 0 ? (float*)workspace : nullptr;
+    float* lse_part = need > 0 ? (float*)((char*)workspace + round256(rows * d * sizeof(float))) : nullptr;
+    fa::DecodeArgs a{q, k, v, o, lse, o_part, lse_part, B, H, Nq, Nk, d, scale, causal != 0};
+    return map_hip(fa::launch_fwd_decode_bf16(a, (hipStream_t)stream));
+}
+
+size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return 0;
+    return decode_workspace_bytes(B, H, Nq, Nk, d);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

@@ -37,6 +37,7 @@
 //   dealt round-robin over the 8 XCDs) so the head's K/V stays in that L2.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
 namespace {
@@ -92,92 +93,6 @@ __device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool r
         qb = bid / heads;
     }
     if (reverse) qb = nqb - 1 - qb;
-}
-
-// K/V tiles in LDS use padded rows instead of a swizzle, so that every
-// operand read of a lane is one base register plus an immediate offset:
-//  * K rows are read 16 rows x 16 bytes per pass (row operands); a row stride
-//    of 2D + 16 bytes puts 16 consecutive rows on 16 distinct 16-byte bank
-//    groups.
-//  * V is read transposed, 4 rows x 64 bytes per pass; a row stride of 2D + 64
-//    bytes puts 4 consecutive rows on 4 distinct 64-byte bank groups.
-// The copy engine writes 64 x 16 contiguous bytes per wave instruction, so the
-// pad chunks are copied too, from an out-of-range offset (zeros, no memory
-// access).
-template <int D, int BC>
-struct PaddedTiles {
-    static constexpr int CH = D / 8;                 // 16-byte chunks of data per row
-    static constexpr int KCH = CH + 1, VCH = CH + 4;
-    static constexpr int KS = KCH * 16, VS = VCH * 16;
-    static constexpr int K_TILE = BC * KS, V_TILE = BC * VS;
-    static_assert(BC * KCH % 64 == 0 && BC * VCH % 64 == 0, "tiles are whole copy blocks");
-};
-
-// Copy of rows [t*BC, t*BC + BC) of one head into a padded tile with RCH
-// chunks per row; the NW waves of the workgroup share the 1 KB copy blocks.
-// The per-lane source offsets within a tile are computed once; a tile adds
-// t * BC rows. Pad chunks read from far past the head (zeros, no memory
-// access; should the sum wrap for a huge head they load real bytes, which is
-// harmless: pad chunks are never read).
-template <int D, int BC, int RCH, int NW>
-struct TileCopy {
-    static constexpr int CH = D / 8, BLKS = BC * RCH / 64, PER = (BLKS + NW - 1) / NW;
-    static constexpr uint32_t kPad = 0xf0000000u;
-    uint32_t off[PER];
-
-    __device__ __forceinline__ TileCopy(int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int pos = (i * NW + wave) * 64 + lane;
-            const int row = pos / RCH, ch = pos % RCH;
-            off[i] = ch < CH ? (uint32_t)(row * D + ch * 8) * 2 : kPad;
-        }
-    }
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, FA_LDS char* base, int t, int wave) const {
-        // Tile offset as an opaque scalar: otherwise loop strength reduction
-        // turns every off[i] into a vector induction variable of its own.
-        const uint32_t toff = __builtin_amdgcn_readfirstlane((uint32_t)t * (BC * D * 2));
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int blk = i * NW + wave;
-            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), off[i] + toff);
-        }
-    }
-};
-
-// Per-lane base offsets of the operand reads in padded tiles.
-//  K operand (S^T = K Q^T, A side): key row l32 (+32 per key block), d = 16c + 8hi .. +7.
-//  V^T operand (O^T = V^T P^T, A side): d = 32db + column, keys 16c + 4(lane/32) + {0..3}
-//  and +8; within a 16-lane group, lane s reads key row s/4 and 4 columns at 4(s%4).
-template <int D, int BC>
-__device__ __forceinline__ int k_base(int lane) {
-    return (lane & 31) * PaddedTiles<D, BC>::KS + (lane >> 5) * 16;
-}
-template <int D, int BC>
-__device__ __forceinline__ int v_base(int lane) {
-    return (4 * (lane >> 5) + ((lane & 15) >> 2)) * PaddedTiles<D, BC>::VS +
-           2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-}
-// K operand i = c * KB + kb of a tile (KB = BC / 32 key blocks).
-template <int D, int BC>
-__device__ __forceinline__ bf16x8 k_operand(const FA_LDS char* kt, int kbase, int i) {
-    constexpr int KB = BC / 32;
-    return *(const FA_LDS bf16x8*)(kt + kbase + (i / KB) * 32 + (i % KB) * 32 * PaddedTiles<D, BC>::KS);
-}
-// V^T operand j = c * DB + db of a tile (DB = D / 32 d blocks, c = 16-key chunk).
-template <int D, int BC>
-__device__ __forceinline__ bf16x8 v_operand(const FA_LDS char* vt, int vbase, int j) {
-    constexpr int DB = D / 32, VS = PaddedTiles<D, BC>::VS;
-    bf16x8 a;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS s16x4*)(vt + vbase + (16 * (j / DB) + 8 * half) * VS + 64 * (j % DB)));
-        const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[4 * half + e] = xb[e];
-    }
-    return a;
 }
 
 template <int D, int BC, int NW, int RB, bool CAUSAL, bool DROPOUT>

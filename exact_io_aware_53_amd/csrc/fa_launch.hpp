@@ -41,6 +41,26 @@ struct BwdArgs {
     float* lse2;       // workspace: fp32 [B,H,N], LSE_i * log2(e)
 };
 
+struct DecodeArgs {
+    const void* q;     // [B, H, Nq, d]
+    const void* k;     // [B, H, Nk, d]
+    const void* v;     // [B, H, Nk, d]
+    void* o;           // [B, H, Nq, d]
+    float* lse;        // [B, H, Nq]
+    float* o_part;     // workspace: fp32 [B*H, S, Nq, d] (S > 1)
+    float* lse_part;   // workspace: fp32 [B*H, S, Nq] (S > 1)
+    int B, H, Nq, Nk, d;
+    float scale;
+    bool causal;
+};
+
+// How the decode forward splits its work: nrb 32-row query blocks, S key
+// chunks of `chunk` keys. Shared by the workspace size and the launch.
+struct DecodeSplit {
+    int nrb, S, chunk;
+};
+DecodeSplit decode_split(int B, int H, int Nq, int Nk);
+
 // Dropout threshold: an element is dropped iff Philox word 0 < thr, thr = ceil(p * 2^32).
 uint32_t dropout_threshold(float p);
 
@@ -48,6 +68,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dropout_mask(uint8_t* mask, int B, int H, int N, int b, int h, float p,
                                uint64_t seed, hipStream_t stream);
 

@@ -71,6 +71,49 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq query rows (the newest positions) against an Nk-row key/value sequence."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool          # query i at key position Nk - Nq + i
+    data_seed: int = 0
+    head_seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.d))
+
+    def io_bytes(self) -> float:
+        """Algorithmic HBM bytes: Q, K, V read once; O and LSE written once (bf16, fp32 LSE)."""
+        return 2.0 * self.B * self.H * self.d * (2 * self.Nq + 2 * self.Nk) + 4.0 * self.B * self.H * self.Nq
+
+
+# Decode-shaped workloads (a new token, and a 16-token block, against a long cache).
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("decode_bf16_b4h32q1k16384d128", 4, 32, 1, 16384, 128, causal=True,
+                       data_seed=1011, head_seed=3011),
+        DecodeWorkload("decode_causal_bf16_b8h16q16k8192d64", 8, 16, 16, 8192, 64, causal=True,
+                       data_seed=1012, head_seed=3012),
+    ]
+}
+
+
+def make_decode_inputs(w: DecodeWorkload):
+    """Q [B,H,Nq,d], K and V [B,H,Nk,d] bf16 CPU tensors (drawn in that order)."""
+    rng = np.random.Generator(np.random.PCG64(w.data_seed))
+    out = {}
+    for name, n in (("q", w.Nq), ("k", w.Nk), ("v", w.Nk)):
+        x = rng.standard_normal((w.B, w.H, n, w.d), dtype=np.float32)
+        out[name] = torch.from_numpy(x).to(torch.bfloat16)
+    return out
+
+
 def normal_tensors(shape, seed: int, count: int, dtype, mults=None):
     """`count` tensors of i.i.d. N(0,1) values (CPU torch tensors of `dtype`)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -94,7 +137,7 @@ def make_inputs(w: Workload, with_grad_out: bool | None = None):
     return dict(zip(names, ts))
 
 
-def sample_heads(w: Workload, count: int):
+def sample_heads(w, count: int):
     """`count` distinct (b, h) pairs drawn from the workload's head seed."""
     rng = np.random.Generator(np.random.PCG64(w.head_seed))
     flat = rng.choice(w.B * w.H, size=min(count, w.B * w.H), replace=False)

@@ -45,8 +45,9 @@
  *   valid once the stream has been synchronised.
  * - Errors: arguments are validated on the host before any HIP call.
  *   FA_ERR_INVALID_ARG  null pointer, B/H/N < 1, dropout_p outside [0, 1),
- *                       non-finite scale, misaligned pointer, too small a
- *                       workspace, B*H*N*d above 2^31 - 1.
+ *                       scale not a positive finite number, misaligned
+ *                       pointer, too small a workspace, B*H*N*d above
+ *                       2^31 - 1.
  *   FA_ERR_UNSUPPORTED  head size d other than 64 or 128 (the caller keeps its
  *                       own fallback, as emergent.sh "How to Enable Flash
  *                       Attention Safely", step 7, advises).
@@ -118,6 +119,36 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  * Returns 0 if an argument is out of range.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Decode-shaped forward, bf16: Nq query rows against Nk key/value rows of the
+ * same head, 1 <= Nq <= Nk, for example the newest tokens against the key/value
+ * cache that inference servers keep (inferensys glossary "FlashAttention",
+ * paragraph on integration with inference servers). Same result as fa_fwd on
+ * that problem (same definition of O and LSE; no dropout). The key range is
+ * split over workgroups and the partial results are merged with the rescaling
+ * of the online softmax.
+ *   q         in : [B, H, Nq, d] bf16
+ *   k, v      in : [B, H, Nk, d] bf16
+ *   o         out: [B, H, Nq, d] bf16
+ *   lse       out: [B, H, Nq] fp32
+ *   causal    nonzero: query row i sits at key position Nk - Nq + i and sees
+ *             keys j <= Nk - Nq + i (bottom-right aligned); zero: every key
+ *   workspace device scratch of fa_fwd_decode_workspace_size(...) bytes,
+ *             256-byte aligned; may be NULL when that size is 0
+ * Errors as for fa_fwd; also FA_ERR_INVALID_ARG when Nq > Nk or the workspace
+ * is missing or too small. The result is bitwise deterministic run to run.
+ */
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device scratch fa_fwd_decode needs: fp32 partial outputs and
+ * log-sum-exps of the key chunks, each region rounded up to 256 bytes. 0 when
+ * the problem is not split, or when an argument is out of range.
+ */
+size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 
 /*
  * Test aid: writes the dropout keep mask Z of head (b, h) as an [N, N] array

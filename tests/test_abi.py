@@ -69,6 +69,8 @@ def test_forward_rejects_invalid_arguments(L, f32):
         assert fwd_call(L, f32=f32, **{name: -3}) == inv
     assert fwd_call(L, f32=f32, scale=float("inf")) == inv
     assert fwd_call(L, f32=f32, scale=float("nan")) == inv
+    assert fwd_call(L, f32=f32, scale=0.0) == inv
+    assert fwd_call(L, f32=f32, scale=-0.125) == inv
     for p in (-0.1, 1.0, 1.5, float("nan")):
         assert fwd_call(L, f32=f32, p=p) == inv
     assert fwd_call(L, f32=f32, B=4096, H=4096, N=4096, d=64) == inv   # too many elements
@@ -92,6 +94,32 @@ def test_backward_rejects_invalid_arguments(L, f32):
         assert call(nulls=(i,)) == fa.FA_ERR_INVALID_ARG
     assert call(p=1.0) == fa.FA_ERR_INVALID_ARG
     assert call(d=80) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_decode_rejects_invalid_arguments(L):
+    inv, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+
+    def call(Nq=1, Nk=4096, d=128, scale=0.1, ws=FAKE * 16, ws_bytes=None, nulls=()):
+        need = L.fa_fwd_decode_workspace_size(2, 4, Nq, Nk, d)
+        ptr = [None if i in nulls else FAKE for i in range(5)]
+        return L.fa_fwd_decode(*ptr, 2, 4, Nq, Nk, d, scale, 1, ws,
+                               need if ws_bytes is None else ws_bytes, None)
+
+    for i in range(5):
+        assert call(nulls=(i,)) == inv
+    assert call(Nq=5, Nk=4) == inv                 # more queries than keys
+    assert call(Nq=0) == inv
+    assert call(scale=0.0) == inv and call(scale=-1.0) == inv and call(scale=float("nan")) == inv
+    assert call(d=96) == uns
+    assert call(ws=None) == inv                     # this shape is split, so it needs scratch
+    assert call(ws_bytes=1) == inv
+    assert call(ws=FAKE * 16 + 64) == inv           # not 256-aligned
+
+
+def test_decode_workspace_size(L):
+    assert L.fa_fwd_decode_workspace_size(1, 1, 1, 100, 64) == 0        # one key chunk: no scratch
+    assert L.fa_fwd_decode_workspace_size(2, 4, 3, 5000, 128) > 0
+    assert L.fa_fwd_decode_workspace_size(1, 1, 5, 4, 64) == 0          # invalid: Nq > Nk
 
 
 def test_dropout_mask_rejects_invalid_arguments(L):

@@ -1,0 +1,108 @@
+"""GPU parity of the decode-shaped forward (fa_fwd_decode) against the fp64 oracle.
+
+Nq query rows sit at key positions Nk - Nq .. Nk - 1 of an Nk-row key/value
+sequence; causal rows see the keys up to their own position. Every row of every
+head is checked on the small shapes, every row of two seeded heads on the full
+decode workloads. Tolerances as for the forward: bf16 O <= 1e-2 (widened only
+where bf16 storage alone exceeds it), LSE <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_53_amd as fa
+import oracle
+from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs, sample_heads, to_f64
+from test_gpu_parity import TOL, o_bound
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()
+
+
+def decode_inputs(B, H, Nq, Nk, d, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [torch.from_numpy(rng.standard_normal((B, H, n, d), dtype=np.float32)).to(torch.bfloat16)
+            for n in (Nq, Nk, Nk)]
+
+
+def check_decode(q, k, v, o, lse, causal, heads, tag=""):
+    Nq, Nk, d = q.shape[2], k.shape[2], q.shape[3]
+    scale = 1.0 / math.sqrt(d)
+    o_c, l_c = o.float().cpu(), lse.cpu()
+    worst_o = worst_l = 0.0
+    for (b, h) in heads:
+        ro, rl = oracle.forward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale, causal,
+                                key_offset=Nk - Nq)
+        go, gl = o_c[b, h].double().numpy(), l_c[b, h].double().numpy()
+        eo = (np.abs(go - ro) / o_bound(ro, TOL["bf16"]["o"], torch.bfloat16)).max() * TOL["bf16"]["o"]
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, np.abs(gl - rl).max())
+    assert worst_o <= TOL["bf16"]["o"], f"{tag} O err {worst_o:.3e}"
+    assert worst_l <= TOL["bf16"]["lse"], f"{tag} LSE err {worst_l:.3e}"
+
+
+# (B, H, Nq, Nk, d): one key; one chunk (Nk <= 128); many chunks with a ragged
+# last one; several 32-row query blocks; Nq = Nk (the full causal square);
+# causal blocks whose early rows see none of the last chunks.
+SHAPES = [(1, 1, 1, 1, 64), (1, 2, 1, 100, 128), (2, 2, 5, 3000, 64), (1, 1, 32, 4099, 128),
+          (1, 2, 33, 777, 64), (1, 1, 70, 70, 128), (2, 1, 17, 5000, 128), (1, 3, 64, 129, 64),
+          (1, 1, 96, 2000, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_small(shape, causal):
+    B, H, Nq, Nk, d = shape
+    q, k, v = decode_inputs(B, H, Nq, Nk, d, 4400 + Nq + Nk + d)
+    o, lse = fa.fwd_decode(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    check_decode(q, k, v, o, lse, causal, [(b, h) for b in range(B) for h in range(H)], str(shape))
+
+
+@pytest.mark.parametrize("name", list(DECODE_WORKLOADS))
+def test_decode_workload(name):
+    w = DECODE_WORKLOADS[name]
+    t = make_decode_inputs(w)
+    o, lse = fa.fwd_decode(t["q"].cuda(), t["k"].cuda(), t["v"].cuda(), causal=w.causal)
+    torch.cuda.synchronize()
+    check_decode(t["q"], t["k"], t["v"], o, lse, w.causal, sample_heads(w, 2), name)
+
+
+def test_decode_is_deterministic():
+    q, k, v = (x.cuda() for x in decode_inputs(2, 4, 3, 6000, 128, 4501))
+    outs = [fa.fwd_decode(q, k, v, causal=True) for _ in range(3)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_decode_single_query_equals_last_row_of_forward():
+    """A one-row decode against the whole sequence is the forward's last causal row."""
+    B, H, N, d = 1, 2, 700, 64
+    q, k, v = (x.cuda() for x in decode_inputs(B, H, N, N, d, 4502))
+    o_f, l_f = fa.fwd(q, k, v, causal=True)
+    o_d, l_d = fa.fwd_decode(q[:, :, -1:].contiguous(), k, v, causal=True)
+    assert (o_d[:, :, 0].float() - o_f[:, :, -1].float()).abs().max().item() <= 2e-2
+    assert (l_d[:, :, 0] - l_f[:, :, -1]).abs().max().item() <= 2e-3
+
+
+def test_decode_outputs_stay_in_bounds():
+    B, H, Nq, Nk, d = 1, 3, 5, 3000, 128
+    q, k, v = (x.cuda() for x in decode_inputs(B, H, Nq, Nk, d, 4503))
+    pad = 4096
+    ob = torch.full((B * H * Nq * d + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((B * H * Nq + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+    need = fa.decode_workspace_size(B, H, Nq, Nk, d)
+    assert need > 0
+    wb = torch.full((need + 2 * 4096,), 7, dtype=torch.uint8, device="cuda")
+    fa.fwd_decode(q, k, v, causal=True, out=ob[pad:-pad].view(B, H, Nq, d),
+                  lse=lb[pad:-pad].view(B, H, Nq), workspace=wb[4096:-4096])
+    torch.cuda.synchronize()
+    for buf, p_ in ((ob, pad), (lb, pad), (wb, 4096)):
+        assert torch.all(buf[:p_] == 7) and torch.all(buf[-p_:] == 7)
