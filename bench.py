@@ -6,8 +6,9 @@ A step is one pass of the path over one batch of synthetic inputs already
 resident in HBM. The default workload is the causal bf16 softmax-stress
 forward (B=2, H=32, N=8192, d=128, Q scaled by 4). The same JSON line also
 carries the forward+backward measurement on the dropout workload
-(B=2, H=16, N=4096, d=64, p=0.1), the roofline of the dominant kernel and the
-CPU oracle's throughput on a bounded sample.
+(B=2, H=16, N=4096, d=64, p=0.1), the decode-shaped forward on its two
+workloads (HBM-bound: GB/s against 8 TB/s), the roofline of the dominant
+kernel and the CPU oracle's throughput on a bounded sample.
 
 FLOPs are counted as 4*B*H*N^2*d for the forward, halved when causal, and
 2.5x that for the backward.
@@ -115,6 +116,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-bwd", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (for HBM counter calibration)")
@@ -207,6 +209,31 @@ def main():
             "tflops_fwd_bwd": round((w2.fwd_flops() + w2.bwd_flops()) / ((tf + tb) * 1e-3) / 1e12, 3),
         }
         del q2, k2, v2, do2, o2, l2, dq2, dk2, dv2, ws
+
+    if not args.no_decode:
+        from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs
+        dec = []
+        for wd in DECODE_WORKLOADS.values():
+            hd = make_decode_inputs(wd)
+            qd, kd, vd = (hd[n].to(dev) for n in ("q", "k", "v"))
+            od = torch.empty_like(qd)
+            ld = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
+            need = fa.decode_workspace_size(wd.B, wd.H, wd.Nq, wd.Nk, wd.d)
+            wsd = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+            def fd():
+                fa.fwd_decode(qd, kd, vd, scale=wd.scale, causal=wd.causal, out=od, lse=ld,
+                              workspace=wsd)
+
+            _, evd = time_launches(fd, args.steps, args.warmup, stream)
+            dms = sum(evd) / len(evd)
+            gbs = wd.io_bytes() / (dms * 1e-3) / 1e9
+            dec.append({"workload": wd.name, "ms": round(dms, 4),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                     "traffic": None, "ideal_io_bytes": wd.io_bytes()}})
+            del qd, kd, vd, od, ld, wsd
+        line["decode"] = dec
 
     if args.calibrate_copy:
         # A plain elementwise copy of known size: reads and writes 2^30 bytes per launch.
