@@ -148,6 +148,7 @@ struct PhiloxRow {
     uint32_t A, B, D0, E1, F;
     uint32_t k0_3, k1_3;   // key of round 4
 
+    PhiloxRow() = default;
     __device__ __forceinline__ PhiloxRow(uint32_t c0, uint32_t c1, uint32_t c2, PhiloxKey key) {
         uint32_t k0 = key.k0, k1 = key.k1;
         const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;   // round 1
