@@ -215,15 +215,19 @@ def main():
         dec = []
         for wd in DECODE_WORKLOADS.values():
             hd = make_decode_inputs(wd)
-            qd, kd, vd = (hd[n].to(dev) for n in ("q", "k", "v"))
-            od = torch.empty_like(qd)
+            names = ("q", "k_pages", "v_pages", "block_table", "seq_lens") if wd.page else ("q", "k", "v")
+            td = [hd[n].to(dev) for n in names]
+            od = torch.empty_like(td[0])
             ld = torch.empty((wd.B, wd.H, wd.Nq), dtype=torch.float32, device=dev)
-            need = fa.decode_workspace_size(wd.B, wd.H, wd.Nq, wd.Nk, wd.d)
-            wsd = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            wsd = torch.empty(1 << 26, dtype=torch.uint8, device=dev)    # above either need
 
             def fd():
-                fa.fwd_decode(qd, kd, vd, scale=wd.scale, causal=wd.causal, out=od, lse=ld,
-                              workspace=wsd)
+                if wd.page:
+                    fa.fwd_decode_paged(*td, scale=wd.scale, causal=wd.causal, out=od, lse=ld,
+                                        workspace=wsd)
+                else:
+                    fa.fwd_decode(*td, scale=wd.scale, causal=wd.causal, out=od, lse=ld,
+                                  workspace=wsd)
 
             _, evd = time_launches(fd, args.steps, args.warmup, stream)
             dms = sum(evd) / len(evd)
@@ -232,7 +236,7 @@ def main():
                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                      "traffic": None, "ideal_io_bytes": wd.io_bytes()}})
-            del qd, kd, vd, od, ld, wsd
+            del td, od, ld, wsd
         line["decode"] = dec
 
     if args.calibrate_copy:

@@ -35,6 +35,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "fa_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "fa_fwd_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "fa_fwd_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "fa_fwd_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "fa_dropout_mask": (_I, [_P, _I, _I, _I, _I, _I, _F, _U64, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -162,6 +164,36 @@ def fwd_decode(q, k, v, scale=None, causal=False, out=None, lse=None, workspace=
     return out, lse
 
 
+def fwd_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, causal=False, out=None,
+                     lse=None, workspace=None):
+    """Decode-shaped forward over a paged cache (bf16): q [B,H,Nq,d]; k_pages, v_pages
+    [num_pages, H, page, d]; block_table [B, max_blocks] int32; seq_lens [B] int32 (GPU)."""
+    B, H, Nq, d = _shape4(q, "q")
+    num_pages, Hk, page, dk = _shape4(k_pages, "k_pages")
+    if _shape4(v_pages, "v_pages") != (num_pages, Hk, page, dk) or Hk != H or dk != d:
+        raise ValueError("k_pages and v_pages must be [num_pages, H, page, d] with q's H and d")
+    for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    max_blocks = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = int(lib().fa_fwd_decode_paged_workspace_size(B, H, Nq, max_blocks, page, d))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().fa_fwd_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                   block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, Nq, max_blocks, page, num_pages, d, scale,
+                                   int(bool(causal)), ws_ptr, ws_bytes, _stream(q.device))
+    _check(st, "fa_fwd_decode_paged")
+    return out, lse
+
+
 def dropout_mask(B, H, N, b, h, dropout_p, seed, device="cuda"):
     """[N, N] uint8 keep mask (1 = kept) of head (b, h), from the device generator."""
     mask = torch.empty((N, N), dtype=torch.uint8, device=device)
@@ -171,5 +203,5 @@ def dropout_mask(B, H, N, b, h, dropout_p, seed, device="cuda"):
     return mask
 
 
-__all__ = ["fwd", "bwd", "fwd_decode", "dropout_mask", "workspace_size", "decode_workspace_size", "lib",
+__all__ = ["fwd", "bwd", "fwd_decode", "fwd_decode_paged", "dropout_mask", "workspace_size", "decode_workspace_size", "lib",
            "FAError", "LIB_PATH", "SIGNATURES"]

@@ -148,6 +148,48 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     return map_hip(fa::launch_fwd_decode_bf16(a, (hipStream_t)stream));
 }
 
+int fa_fwd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                        int B, int H, int Nq, int max_blocks, int page_size, int num_pages, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes_, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(lse) ||
+        ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
+        return FA_ERR_INVALID_ARG;
+    if (page_size < 32 || page_size % 32 != 0 || max_blocks < 1 || num_pages < 1)
+        return FA_ERR_INVALID_ARG;
+    if ((long long)max_blocks * page_size > kMaxElems) return FA_ERR_INVALID_ARG;
+    const int max_keys = max_blocks * page_size;
+    if (!decode_shape_ok(B, H, Nq, max_keys, 1)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * Nq * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const size_t need = decode_workspace_bytes(B, H, Nq, max_keys, d);
+    if (need > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes_ < need)
+            return FA_ERR_INVALID_ARG;
+    }
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, max_keys);
+    const size_t rows = (size_t)B * H * sp.S * Nq;
+    float* o_part = need > 0 ? (float*)workspace : nullptr;
+    float* lse_part = need > 0 ? (float*)((char*)workspace + round256(rows * d * sizeof(float))) : nullptr;
+    fa::DecodeArgs a{q, k_pages, v_pages, o, lse, o_part, lse_part, B, H, Nq, max_keys, d, scale, causal != 0};
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks;
+    a.page = page_size;
+    a.num_pages = num_pages;
+    return map_hip(fa::launch_fwd_decode_bf16(a, (hipStream_t)stream));
+}
+
+size_t fa_fwd_decode_paged_workspace_size(int B, int H, int Nq, int max_blocks, int page_size, int d) {
+    if (page_size < 32 || page_size % 32 != 0 || max_blocks < 1) return 0;
+    if ((long long)max_blocks * page_size > kMaxElems) return 0;
+    const int max_keys = max_blocks * page_size;
+    if (!decode_shape_ok(B, H, Nq, max_keys, 1) || d < 1) return 0;
+    return decode_workspace_bytes(B, H, Nq, max_keys, d);
+}
+
 size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
     if (!decode_shape_ok(B, H, Nq, Nk, d)) return 0;
     return decode_workspace_bytes(B, H, Nq, Nk, d);

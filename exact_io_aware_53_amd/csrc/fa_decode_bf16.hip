@@ -36,17 +36,20 @@ constexpr int kDecChunk = kDecNW * kDecTile;   // key chunks are multiples of th
 
 struct DecodeParams {
     const __bf16* q;
-    const __bf16* k;
+    const __bf16* k;          // contiguous: [heads, Nk, D]; paged: the page pool [num_pages, H, page, D]
     const __bf16* v;
     __bf16* o;
     float* lse;
     float* o_part;     // [heads, S, Nq, D] fp32 partial outputs (S > 1)
     float* lse_part;   // [heads, S, Nq] fp32 partial log-sum-exp (S > 1)
+    const int* block_table;   // paged: [B, max_blocks] page of each logical block
+    const int* seq_lens;      // paged: [B] key count of each sequence
     int Nq, Nk, nrb, S, chunk;
+    int H, max_blocks, page, num_pages;
     float sl2;         // scale * log2(e)
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeParams p) {
     constexpr int DB = D / 32, NCD = D / 16;
@@ -63,11 +66,29 @@ void decode_split_kernel(DecodeParams p) {
     const int bid = blockIdx.x;
     const int s = bid % p.S, rest = bid / p.S;
     const int rb = rest % p.nrb, bh = rest / p.nrb;
-    const int Nq = p.Nq, Nk = p.Nk;
+    const int Nq = p.Nq;
+    const int b = bh / p.H, h = bh - b * p.H;
+    // Keys of this sequence (paged: its own length, clamped to the block table's reach).
+    const int Nk = PAGED ? min(max(p.seq_lens[b], 0), p.max_blocks * p.page) : p.Nk;
     const int r0 = rb * 32, my_q = r0 + l32;
     const auto rs_q = make_rsrc(p.q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 2);
     const auto rs_k = make_rsrc(p.k + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
     const auto rs_v = make_rsrc(p.v + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
+    // Paged: the 32-key tile at key0 lies in one page (pages are whole tiles).
+    // A block-table entry outside [0, num_pages) reads as zeros.
+    struct TileSrc {
+        __amdgpu_buffer_rsrc_t k, v;
+        int row;                       // first row of the tile inside the resource
+    };
+    auto tile_src = [&](int key0) {
+        if (!PAGED) return TileSrc{rs_k, rs_v, key0};
+        const int lb = key0 / p.page;
+        const int pid = p.block_table[(size_t)b * p.max_blocks + lb];
+        const bool ok = pid >= 0 && pid < p.num_pages;
+        const size_t base = ((size_t)(ok ? pid : 0) * p.H + h) * p.page * D;
+        const uint32_t bytes = ok ? (uint32_t)p.page * D * 2 : 0u;
+        return TileSrc{make_rsrc(p.k + base, bytes), make_rsrc(p.v + base, bytes), key0 - lb * p.page};
+    };
 
     // Keys of this chunk that any row of the block may see.
     const int off = Nk - Nq;                                        // key position of query row 0
@@ -95,13 +116,14 @@ void decode_split_kernel(DecodeParams p) {
     const int vbase = v_base<D, kDecTile>(lane);
     // Tile t of this wave covers keys k_lo + 32 (wave + 4t) ...
     auto key0 = [&](int t) { return k_lo + kDecTile * (wave + kDecNW * t); };
-    auto load_k = [&](int t, bf16x8 (&kr)[NCD]) {
-        const int key = key0(t) + l32;
+    auto load_kv = [&](int t, bf16x8 (&kr)[NCD]) {
+        const TileSrc src = tile_src(key0(t));
+        const int row = src.row + l32;
 #pragma unroll
         for (int c = 0; c < NCD; ++c)
-            kr[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_k, (uint32_t)(key * D + 16 * c + 8 * hi) * 2));
+            kr[c] = __builtin_bit_cast(bf16x8, buffer_load16(src.k, (uint32_t)(row * D + 16 * c + 8 * hi) * 2));
+        vcopy.issue(src.v, vw + (t & 1) * VT, src.row / kDecTile, 0);
     };
-    auto load_v = [&](int t) { vcopy.issue(rs_v, vw + (t & 1) * VT, key0(t) / kDecTile, 0); };
 
     const int nt_w = ntiles > wave ? (ntiles - wave + kDecNW - 1) / kDecNW : 0;   // this wave's tiles
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -109,10 +131,7 @@ void decode_split_kernel(DecodeParams p) {
     // register sets swap roles from tile to tile, so no copy waits on a load).
     auto tile = [&](int t, bf16x8 (&kc)[NCD], bf16x8 (&kn)[NCD]) {
         wait_vmem();                      // K registers and V tile t have landed
-        if (t + 1 < nt_w) {
-            load_k(t + 1, kn);
-            load_v(t + 1);
-        }
+        if (t + 1 < nt_w) load_kv(t + 1, kn);
         // S^T = K Q^T: element r is key key0(t) + 8(r/4) + 4hi + r%4 against row my_q.
         f32x16 sc;
 #pragma unroll
@@ -163,10 +182,7 @@ void decode_split_kernel(DecodeParams p) {
                                                                   pb[j / DB], oacc[j % DB], 0, 0, 0);
     };
     bf16x8 ka[NCD], kb[NCD];
-    if (nt_w > 0) {
-        load_k(0, ka);
-        load_v(0);
-    }
+    if (nt_w > 0) load_kv(0, ka);
     for (int t = 0; t < nt_w; t += 2) {
         tile(t, ka, kb);
         if (t + 1 < nt_w) tile(t + 1, kb, ka);
@@ -264,16 +280,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int r
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, op[e], acc[e]);
     }
-    const float inv = 1.0f / l;
+    // A row that sees no key at all (paged, causal, sequence shorter than Nq)
+    // gets O = 0 and LSE = -inf.
+    const float inv = m == -INFINITY ? 0.0f : 1.0f / l;
     __bf16* orow = p.o + (size_t)row * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) orow[e] = (__bf16)(acc[e] * inv);
-    if (lane == 0) p.lse[row] = m + fast_log2(l) * kLn2;
+    if (lane == 0) p.lse[row] = m == -INFINITY ? -INFINITY : m + fast_log2(l) * kLn2;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
-    const DecodeSplit sp = decode_split(a.B, a.H, a.Nq, a.Nk);
+    const DecodeSplit sp = decode_split(a.B, a.H, a.Nq, PAGED ? a.max_blocks * a.page : a.Nk);
     DecodeParams p{};
     p.q = (const __bf16*)a.q;
     p.k = (const __bf16*)a.k;
@@ -282,15 +300,21 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     p.lse = a.lse;
     p.o_part = a.o_part;
     p.lse_part = a.lse_part;
+    p.block_table = a.block_table;
+    p.seq_lens = a.seq_lens;
     p.Nq = a.Nq;
     p.Nk = a.Nk;
+    p.H = a.H;
+    p.max_blocks = a.max_blocks;
+    p.page = a.page;
+    p.num_pages = a.num_pages;
     p.nrb = sp.nrb;
     p.S = sp.S;
     p.chunk = sp.chunk;
     p.sl2 = a.scale * kLog2e;
     const int heads = a.B * a.H;
-    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3(heads * sp.nrb * sp.S), dim3(kDecNW * 64), 0, st,
-                       p);
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, PAGED>), dim3(heads * sp.nrb * sp.S), dim3(kDecNW * 64),
+                       0, st, p);
     if (sp.S > 1) {
         const int rows = heads * a.Nq;
         hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, st, p, rows);
@@ -318,8 +342,12 @@ DecodeSplit decode_split(int B, int H, int Nq, int Nk) {
 }
 
 hipError_t launch_fwd_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-    if (a.d == 64) return a.causal ? launch<64, true>(a, st) : launch<64, false>(a, st);
-    return a.causal ? launch<128, true>(a, st) : launch<128, false>(a, st);
+    if (a.block_table) {
+        if (a.d == 64) return a.causal ? launch<64, true, true>(a, st) : launch<64, false, true>(a, st);
+        return a.causal ? launch<128, true, true>(a, st) : launch<128, false, true>(a, st);
+    }
+    if (a.d == 64) return a.causal ? launch<64, true, false>(a, st) : launch<64, false, false>(a, st);
+    return a.causal ? launch<128, true, false>(a, st) : launch<128, false, false>(a, st);
 }
 
 }  // namespace fa

@@ -52,6 +52,12 @@ struct DecodeArgs {
     int B, H, Nq, Nk, d;
     float scale;
     bool causal;
+    // Paged key/value (block_table != nullptr): k and v are page pools
+    // [num_pages, H, page, d]; sequence b's key row j lives in page
+    // block_table[b * max_blocks + j / page], row j % page; seq_lens[b] keys.
+    const int* block_table = nullptr;
+    const int* seq_lens = nullptr;
+    int max_blocks = 0, page = 0, num_pages = 0;
 };
 
 // How the decode forward splits its work: nrb 32-row query blocks, S key

@@ -83,6 +83,7 @@ class DecodeWorkload:
     causal: bool          # query i at key position Nk - Nq + i
     data_seed: int = 0
     head_seed: int = 0
+    page: int = 0         # > 0: K/V stored in shuffled pages of this many rows
 
     @property
     def scale(self) -> float:
@@ -100,17 +101,34 @@ DECODE_WORKLOADS = {
                        data_seed=1011, head_seed=3011),
         DecodeWorkload("decode_causal_bf16_b8h16q16k8192d64", 8, 16, 16, 8192, 64, causal=True,
                        data_seed=1012, head_seed=3012),
+        DecodeWorkload("decode_paged128_bf16_b4h32q1k16384d128", 4, 32, 1, 16384, 128, causal=True,
+                       data_seed=1011, head_seed=3011, page=128),
     ]
 }
 
 
 def make_decode_inputs(w: DecodeWorkload):
-    """Q [B,H,Nq,d], K and V [B,H,Nk,d] bf16 CPU tensors (drawn in that order)."""
+    """Q [B,H,Nq,d], K and V [B,H,Nk,d] bf16 CPU tensors (drawn in that order). Paged
+    workloads also get the page pools k_pages, v_pages [B*Nk/page, H, page, d], holding
+    the same rows in a seeded random page order, the block table [B, Nk/page] (int32)
+    and seq_lens [B] (int32, all Nk)."""
     rng = np.random.Generator(np.random.PCG64(w.data_seed))
     out = {}
     for name, n in (("q", w.Nq), ("k", w.Nk), ("v", w.Nk)):
         x = rng.standard_normal((w.B, w.H, n, w.d), dtype=np.float32)
         out[name] = torch.from_numpy(x).to(torch.bfloat16)
+    if w.page:
+        nb = w.Nk // w.page
+        perm = torch.from_numpy(rng.permutation(w.B * nb).astype(np.int64))
+        table = perm.view(w.B, nb)
+        for name in ("k", "v"):
+            blocks = out[name].view(w.B, w.H, nb, w.page, w.d).permute(0, 2, 1, 3, 4).reshape(
+                w.B * nb, w.H, w.page, w.d)
+            pool = torch.empty_like(blocks)
+            pool[table.reshape(-1)] = blocks
+            out[name + "_pages"] = pool
+        out["block_table"] = table.to(torch.int32).contiguous()
+        out["seq_lens"] = torch.full((w.B,), w.Nk, dtype=torch.int32)
     return out
 
 

@@ -151,6 +151,32 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
 size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 
 /*
+ * Decode-shaped forward over a paged key/value cache, bf16: the kernel side of
+ * paged KV-cache management (inferensys glossary "FlashAttention", related term
+ * PagedAttention: the cache lives in non-contiguous fixed-size blocks). Sequence
+ * b has seq_lens[b] keys; its key row j is row (j % page_size) of page
+ * block_table[b * max_blocks + j / page_size]. Otherwise as fa_fwd_decode, with
+ * Nk = seq_lens[b] per sequence (bottom-right causal alignment per sequence).
+ *   k_pages, v_pages in : [num_pages, H, page_size, d] bf16 page pools
+ *   block_table      in : [B, max_blocks] int32, device memory
+ *   seq_lens         in : [B] int32, device memory; values are clamped to
+ *                         [0, max_blocks * page_size]
+ *   page_size           : a multiple of 32 (32-key tiles never straddle pages)
+ * The tables are read on the device and not validated there beyond this: a
+ * table entry outside [0, num_pages) reads as zeros (no memory access). A
+ * query row that sees no key (a sequence shorter than Nq, causal; or empty)
+ * gets O = 0 and LSE = -inf.
+ */
+int fa_fwd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                        int B, int H, int Nq, int max_blocks, int page_size, int num_pages, int d,
+                        float scale, int causal, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes fa_fwd_decode_paged needs (0 when not split or invalid). */
+size_t fa_fwd_decode_paged_workspace_size(int B, int H, int Nq, int max_blocks, int page_size, int d);
+
+/*
  * Test aid: writes the dropout keep mask Z of head (b, h) as an [N, N] array
  * of bytes (1 = kept, 0 = dropped) into device memory `mask`, using the same
  * device generator as the attention kernels. Causal masking is not applied.

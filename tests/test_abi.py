@@ -116,6 +116,23 @@ def test_decode_rejects_invalid_arguments(L):
     assert call(ws=FAKE * 16 + 64) == inv           # not 256-aligned
 
 
+def test_decode_paged_rejects_invalid_arguments(L):
+    inv = fa.FA_ERR_INVALID_ARG
+
+    def call(page=64, max_blocks=64, nulls=(), ws_bytes=None, Nq=1):
+        need = L.fa_fwd_decode_paged_workspace_size(2, 4, Nq, max_blocks, page, 128)
+        ptr = [None if i in nulls else FAKE for i in range(7)]
+        return L.fa_fwd_decode_paged(*ptr, 2, 4, Nq, max_blocks, page, 100, 128, 0.1, 1, FAKE * 16,
+                                     need if ws_bytes is None else ws_bytes, None)
+
+    for i in range(7):
+        assert call(nulls=(i,)) == inv
+    assert call(page=48) == inv and call(page=16) == inv     # not a multiple of 32
+    assert call(max_blocks=0) == inv
+    assert call(Nq=64 * 64 + 1) == inv                          # more queries than the table reaches
+    assert call(ws_bytes=1) == inv
+
+
 def test_decode_workspace_size(L):
     assert L.fa_fwd_decode_workspace_size(1, 1, 1, 100, 64) == 0        # one key chunk: no scratch
     assert L.fa_fwd_decode_workspace_size(2, 4, 3, 5000, 128) > 0
