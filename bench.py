@@ -6,9 +6,11 @@ A step is one pass of the path over one batch of synthetic inputs already
 resident in HBM. The default workload is the causal bf16 softmax-stress
 forward (B=2, H=32, N=8192, d=128, Q scaled by 4). The same JSON line also
 carries the forward+backward measurement on the dropout workload
-(B=2, H=16, N=4096, d=64, p=0.1), the decode-shaped forward on its two
-workloads (HBM-bound: GB/s against 8 TB/s), the roofline of the dominant
-kernel and the CPU oracle's throughput on a bounded sample.
+(B=2, H=16, N=4096, d=64, p=0.1; the backward in both its fused atomic form
+and its two-pass deterministic form), the backward at the default workload's
+shape, the decode-shaped forward on its three workloads (HBM-bound: GB/s
+against 8 TB/s), the roofline of the dominant kernel and the CPU oracle's
+throughput on a bounded sample.
 
 FLOPs are counted as 4*B*H*N^2*d for the forward, halved when causal, and
 2.5x that for the backward.
@@ -199,16 +201,43 @@ def main():
             fa.bwd(q2, k2, v2, o2, l2, do2, scale=w2.scale, causal=True, dropout_p=w2.dropout_p,
                    seed=w2.dropout_seed, dq=dq2, dk=dk2, dv=dv2, workspace=ws)
 
+        def b2_det():
+            fa.bwd(q2, k2, v2, o2, l2, do2, scale=w2.scale, causal=True, dropout_p=w2.dropout_p,
+                   seed=w2.dropout_seed, dq=dq2, dk=dk2, dv=dv2, workspace=ws, deterministic=True)
+
         f2()
         tf, _ = time_launches(f2, args.steps, args.warmup, stream)
         tb, _ = time_launches(b2, args.steps, args.warmup, stream)
+        td, _ = time_launches(b2_det, args.steps, args.warmup, stream)
         line["fwd_bwd"] = {
             "workload": w2.name, "ms_fwd": round(tf, 4), "ms_bwd": round(tb, 4),
             "tflops_fwd": round(w2.fwd_flops() / (tf * 1e-3) / 1e12, 3),
             "tflops_bwd": round(w2.bwd_flops() / (tb * 1e-3) / 1e12, 3),
             "tflops_fwd_bwd": round((w2.fwd_flops() + w2.bwd_flops()) / ((tf + tb) * 1e-3) / 1e12, 3),
+            # two-pass deterministic form: the dropout mask is generated twice
+            "ms_bwd_deterministic": round(td, 4),
+            "tflops_bwd_deterministic": round(w2.bwd_flops() / (td * 1e-3) / 1e12, 3),
         }
         del q2, k2, v2, do2, o2, l2, dq2, dk2, dv2, ws
+
+        # The backward at the forward workload's shape (no dropout: the two-pass
+        # form, no atomics), on the same seeded Q, K, V plus a seeded dO.
+        h3 = make_inputs(w, with_grad_out=True)
+        do3 = h3["do"].to(dev)
+        del h3
+        dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws3 = torch.empty(fa.workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+        fwd_step()
+
+        def b3():
+            fa.bwd(q, k, v, o, lse, do3, scale=w.scale, causal=w.causal, dropout_p=w.dropout_p,
+                   seed=w.dropout_seed, dq=dq3, dk=dk3, dv=dv3, workspace=ws3)
+
+        t3, _ = time_launches(b3, args.steps, args.warmup, stream)
+        line["bwd"] = {"workload": w.name, "ms_bwd": round(t3, 4),
+                       "tflops_bwd": round(w.bwd_flops() / (t3 * 1e-3) / 1e12, 3),
+                       "frac": round(w.bwd_flops() / (t3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del do3, dq3, dk3, dv3, ws3
 
     if not args.no_decode:
         from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs

@@ -32,6 +32,7 @@ SIGNATURES = {
     "fa_fwd_f32": (_I, _FWD_ARGS),
     "fa_bwd": (_I, _BWD_ARGS),
     "fa_bwd_f32": (_I, _BWD_ARGS),
+    "fa_bwd_deterministic": (_I, _BWD_ARGS),
     "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "fa_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "fa_fwd_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
@@ -111,8 +112,10 @@ def workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 
 def bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0,
-        dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass: returns (dQ, dK, dV) in the input dtype."""
+        dq=None, dk=None, dv=None, workspace=None, deterministic=False):
+    """Backward pass: returns (dQ, dK, dV) in the input dtype. deterministic=True
+    (bf16 only) computes dQ in its own pass, without atomics, so that the result
+    is bitwise reproducible."""
     shp = _shape4(q, "q")
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
         if _shape4(t, n) != shp or t.dtype != q.dtype:
@@ -125,13 +128,16 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0,
     need = workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = _entry(q.dtype, "fa_bwd")(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+    if deterministic and q.dtype != torch.bfloat16:
+        raise ValueError("the deterministic backward takes bfloat16 tensors")
+    name = "fa_bwd_deterministic" if deterministic else "fa_bwd"
+    st = _entry(q.dtype, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                    dv.data_ptr(), B, H, N, d, scale, int(bool(causal)),
                                    float(dropout_p), int(seed) & (2**64 - 1),
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(q.device))
-    _check(st, "fa_bwd")
+    _check(st, name)
     return dq, dk, dv
 
 

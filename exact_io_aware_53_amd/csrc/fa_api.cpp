@@ -72,7 +72,8 @@ int fwd_common(bool bf16, const void* q, const void* k, const void* v, void* o, 
 int bwd_common(bool bf16, const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv,
                int B, int H, int N, int d, float scale, int causal, float dropout_p,
-               uint64_t seed, void* workspace, size_t ws_bytes, void* stream) {
+               uint64_t seed, void* workspace, size_t ws_bytes, void* stream,
+               bool deterministic = false) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
         return FA_ERR_INVALID_ARG;
     const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
@@ -87,7 +88,7 @@ int bwd_common(bool bf16, const void* q, const void* k, const void* v, const voi
     float* dsum = (float*)((char*)workspace + round256(rows * d * sizeof(float)));
     float* lse2 = (float*)((char*)dsum + round256(rows * sizeof(float)));
     fa::BwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, dout, lse,
-                  dq, dk, dv, dq_acc, dsum, lse2};
+                  dq, dk, dv, dq_acc, dsum, lse2, deterministic};
     hipStream_t s = (hipStream_t)stream;
     return map_hip(bf16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
@@ -115,6 +116,15 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* stream) {
     return bwd_common(true, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
                       dropout_p, seed, workspace, workspace_bytes_, stream);
+}
+
+int fa_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, float scale, int causal,
+                         float dropout_p, uint64_t seed, void* workspace,
+                         size_t workspace_bytes_, void* stream) {
+    return bwd_common(true, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                      dropout_p, seed, workspace, workspace_bytes_, stream, true);
 }
 
 int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,

@@ -31,6 +31,9 @@
 //   with global atomics. A last pass converts that accumulator to bf16.
 // * LDS rows are XOR-swizzled in 16-byte chunks (chunk_swizzle) so that both
 //   access shapes, row operands and transposed reads, are conflict-free.
+// * Two-pass form (DQ = false): the same kernel without the dQ products, then
+//   bwd_dq_kernel for dQ. No atomics, so bitwise deterministic; without
+//   dropout it is also the faster form and the default.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -72,7 +75,10 @@ __device__ __forceinline__ bf16x8 tr_read(const FA_LDS char* base, int off0, int
     return a;
 }
 
-template <int D, int BQ, bool CAUSAL, bool DROPOUT>
+// DQ = false: the key/value side only (dK, dV); dQ then comes from its own
+// pass (bwd_dq_kernel). Without the dQ products the Q/dO tiles are
+// double-buffered and one barrier per tile remains.
+template <int D, int BQ, bool CAUSAL, bool DROPOUT, bool DQ>
 __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     constexpr int CH = D / 8;
     constexpr int QB = BQ / 32;        // 32-row query blocks per tile
@@ -87,12 +93,13 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     constexpr int DQ_ATOMICS = (QB * DB / kNW) * 16;   // dQ atomics per lane per tile
     static_assert(DQ_ATOMICS <= 63, "vmcnt holds at most 63");
 
-    __shared__ __attribute__((aligned(1024))) char q_s[TILE];
-    __shared__ __attribute__((aligned(1024))) char do_s[TILE];
-    __shared__ __attribute__((aligned(1024))) char k_s[kBKV * D * 2];
-    __shared__ __attribute__((aligned(1024))) char dst_s[kBKV * BQ * 2];
-    __shared__ float lse_s[BQ];
-    __shared__ float dsum_s[BQ];
+    constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
+    __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
+    __shared__ __attribute__((aligned(1024))) char do_s[NBUF * TILE];
+    __shared__ __attribute__((aligned(1024))) char k_s[DQ ? kBKV * D * 2 : 16];
+    __shared__ __attribute__((aligned(1024))) char dst_s[DQ ? kBKV * BQ * 2 : 16];
+    __shared__ float lse_s[NBUF * BQ];
+    __shared__ float dsum_s[NBUF * BQ];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -163,12 +170,14 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
         vt[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_v, off));
     }
     // All 128 keys of the block into LDS for the dQ products.
+    if (DQ) {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-        const int blk = i * kNW + wave, pos = blk * 64 + lane;
-        const int row = pos / CH, sw = pos % CH;
-        buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
-                        (uint32_t)((j0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2);
+        for (int i = 0; i < KLOADS; ++i) {
+            const int blk = i * kNW + wave, pos = blk * 64 + lane;
+            const int row = pos / CH, sw = pos % CH;
+            buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
+                            (uint32_t)((j0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2);
+        }
     }
 
     f32x16 dva[DB], dka[DB];
@@ -177,20 +186,20 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dva[i][r] = dka[i][r] = 0.0f;
 
-    auto issue_tile = [&](int i0) {
+    auto issue_tile = [&](int i0, int buf) {
 #pragma unroll
         for (int i = 0; i < QLOADS; ++i) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
             const uint32_t off = (uint32_t)((i0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2;
-            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + blk * 1024), off);
-            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + blk * 1024), off);
+            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + buf * TILE + blk * 1024), off);
+            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), off);
         }
         if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)lse_s, 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)(lse_s + buf * BQ), 4,
                                                      (uint32_t)(i0 + lane) * 4, 0, 0, 0);
         if (wave == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)dsum_s, 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)(dsum_s + buf * BQ), 4,
                                                      (uint32_t)(i0 + lane) * 4, 0, 0, 0);
     };
 
@@ -201,21 +210,28 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     // those stay in that XCD's L2.
     const int i_first = CAUSAL ? j0 : 0;         // j0 < N, so i_first <= i_last
     const int i_last = (N - 1) / BQ * BQ;
-    issue_tile(i_last);
+    issue_tile(i_last, 0);
 
     for (int i0 = i_last; i0 >= i_first; i0 -= BQ) {
+        const int buf = DQ ? 0 : ((i_last - i0) / BQ) & 1;
         // Vector-memory operations retire in issue order, and the previous tile
         // issued this tile's loads before exactly DQ_ATOMICS atomics per lane:
         // waiting until at most that many remain waits for the loads only.
-        if (i0 == i_last)
+        if (!DQ || i0 == i_last)
             wait_vmem();
         else
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DQ_ATOMICS) : "memory");
         __syncthreads();
+        if (!DQ && i0 > i_first) issue_tile(i0 - BQ, buf ^ 1);   // the other buffer: read last tile
+        const FA_LDS char* const qT = qL + buf * TILE;
+        const FA_LDS char* const doT = doL + buf * TILE;
+        const float* const lse_t = lse_s + buf * BQ;
+        const float* const dsum_t = dsum_s + buf * BQ;
 
         const bool skip = CAUSAL && kw > i0 + BQ - 1;    // every query of the tile precedes our keys
         if (skip) {
             // this wave's rows of dS^T are zero for this tile
+            if (DQ)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -232,9 +248,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                 for (int c = 0; c < NCD; ++c) {
                     const int o = roff[c] + qb * 32 * ROW;
                     s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *(const FA_LDS bf16x8*)(qL + o), kt[c], s[qb], 0, 0, 0);
+                        *(const FA_LDS bf16x8*)(qT + o), kt[c], s[qb], 0, 0, 0);
                     dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *(const FA_LDS bf16x8*)(doL + o), vt[c], dp[qb], 0, 0, 0);
+                        *(const FA_LDS bf16x8*)(doT + o), vt[c], dp[qb], 0, 0, 0);
                 }
             }
             // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
@@ -242,16 +258,19 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    s[qb][r] = fmaf(s[qb][r], p.sl2, -lse_s[qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)]);
+                    s[qb][r] = fmaf(s[qb][r], p.sl2, -lse_t[qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)]);
             // Only tiles that cross the diagonal or a ragged end hold masked elements.
+            // Element (qb, r) is query row i0 + 4hi + e with e = 32qb + 8(r/4) + r%4, a
+            // compile-time offset; the bounds are moved to the lane's side.
             if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
+                const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
+                const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        const bool live = qi < N && my_key < N && (!CAUSAL || my_key <= qi);
-                        if (!live) s[qb][r] = -INFINITY;
+                        const int e = qb * 32 + 8 * (r >> 2) + (r & 3);
+                        if (e < e_lo || e >= e_hi) s[qb][r] = -INFINITY;
                     }
             }
 #pragma unroll
@@ -267,7 +286,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                                                         (uint32_t)my_key, p.key);
                         z = w >= p.thr ? p.inv_keep : 0.0f;
                     }
-                    const float ds = pr * fmaf(dp[qb][r], z, -dsum_s[qrow]);
+                    const float ds = pr * fmaf(dp[qb][r], z, -dsum_t[qrow]);
                     s[qb][r] = pr * z;      // P Z' for dV
                     dp[qb][r] = ds;         // dS
                 }
@@ -283,13 +302,14 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
-                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(doL, o0, o1), bp,
+                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(doT, o0, o1), bp,
                                                                      dva[db], 0, 0, 0);
-                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qL, o0, o1), bs,
+                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qT, o0, o1), bs,
                                                                      dka[db], 0, 0, 0);
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
+            if (DQ)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -300,8 +320,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
                     *(FA_LDS u32x2*)(dsL + tile_offset<BQ / 8>(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi)) = w;
                 }
         }
+        if (!DQ) continue;
         __syncthreads();
-        if (i0 > i_first) issue_tile(i0 - BQ);    // Q/dO/LSE/D are not read again this tile
+        if (i0 > i_first) issue_tile(i0 - BQ, 0);   // Q/dO/LSE/D are not read again this tile
 
         // dQ_tile = dS K over the block's 128 keys, 32x32 blocks dealt to the waves
 #pragma unroll
@@ -345,9 +366,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     }
 }
 
-// D_i = <dO_i, O_i> in fp32, LSE_i in log2 units, and a zeroed dQ
+// D_i = <dO_i, O_i> in fp32, LSE_i in log2 units, and (ZERO) a zeroed dQ
 // accumulator; 8 lanes per row.
-template <int D>
+template <int D, bool ZERO>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __bf16* dout,
                                                       const float* lse, float* dsum, float* lse2,
                                                       float* dq_acc, int rows) {
@@ -363,8 +384,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __b
             const bf16x8 g = *(const bf16x8*)(dout + base + c);
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)g[i], acc);
-            *(f32x4*)(dq_acc + base + c) = f32x4{0.f, 0.f, 0.f, 0.f};
-            *(f32x4*)(dq_acc + base + c + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ZERO) {
+                *(f32x4*)(dq_acc + base + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+                *(f32x4*)(dq_acc + base + c + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
     acc += __shfl_xor(acc, 1);
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, __bf1
     *(bf16x8*)(dq + 8 * i) = r;
 }
 
-template <int D, bool CAUSAL, bool DROPOUT>
+template <int D, bool CAUSAL, bool DROPOUT, bool DQ>
 hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
     BwdParamsB p{};
     p.q = (const __bf16*)a.q;
@@ -412,23 +435,40 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
     p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 64, CAUSAL, DROPOUT>), dim3(p.heads * p.nkb),
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 64, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
                        dim3(kNW * 64), 0, st, p);
     return hipGetLastError();
+}
+
+template <int D, bool DQ>
+hipError_t launch_kv(const BwdArgs& a, hipStream_t st) {
+    const bool drop = dropout_threshold(a.s.dropout_p) != 0;
+    if (a.s.causal)
+        return drop ? launch_main<D, true, true, DQ>(a, st) : launch_main<D, true, false, DQ>(a, st);
+    return drop ? launch_main<D, false, true, DQ>(a, st) : launch_main<D, false, false, DQ>(a, st);
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     const int rows = a.s.B * a.s.H * a.s.N;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((rows + 31) / 32), dim3(256), 0, st,
+    // Without dropout the two-pass form is also the faster one (the dQ atomics
+    // cost more than recomputing S and dP once more); with dropout the Philox
+    // mask would be generated twice, and the fused form wins.
+    const bool drop = dropout_threshold(a.s.dropout_p) != 0;
+    if (a.deterministic || !drop) {
+        // dK, dV from the key-side pass; dQ from its own query-side pass. No
+        // atomics: every output element is written by one lane in a fixed order.
+        hipLaunchKernelGGL((bwd_pre_kernel<D, false>), dim3((rows + 31) / 32), dim3(256), 0, st,
+                           (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.dsum, a.lse2,
+                           a.dq_accum, rows);
+        const hipError_t e = launch_kv<D, false>(a, st);
+        if (e != hipSuccess) return e;
+        return launch_bwd_dq_bf16(a, st);
+    }
+    hipLaunchKernelGGL((bwd_pre_kernel<D, true>), dim3((rows + 31) / 32), dim3(256), 0, st,
                        (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.dsum, a.lse2,
                        a.dq_accum, rows);
-    const bool drop = dropout_threshold(a.s.dropout_p) != 0;
-    hipError_t e;
-    if (a.s.causal)
-        e = drop ? launch_main<D, true, true>(a, st) : launch_main<D, true, false>(a, st);
-    else
-        e = drop ? launch_main<D, false, true>(a, st) : launch_main<D, false, false>(a, st);
+    const hipError_t e = launch_kv<D, true>(a, st);
     if (e != hipSuccess) return e;
     const size_t n8 = (size_t)rows * D / 8;
     hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,

@@ -39,6 +39,7 @@ struct BwdArgs {
     float* dq_accum;   // workspace: fp32 [B,H,N,d]
     float* dsum;       // workspace: fp32 [B,H,N], D_i = <dO_i, O_i>
     float* lse2;       // workspace: fp32 [B,H,N], LSE_i * log2(e)
+    bool deterministic = false;   // dQ from its own pass instead of atomics (bf16 only)
 };
 
 struct DecodeArgs {
@@ -72,6 +73,8 @@ uint32_t dropout_threshold(float p);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+// The query-side pass of the deterministic backward: dQ only (bf16 path).
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_decode_bf16(const DecodeArgs& a, hipStream_t stream);

@@ -94,13 +94,31 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * gradient dO, writes dQ, dK, dV ([B, H, N, d] bf16).
  *   workspace        device scratch of at least fa_bwd_workspace_size(B,H,N,d)
  *                    bytes, 256-byte aligned; contents on entry are ignored.
- * dQ is accumulated with fp32 atomics, so its last bits may vary run to run.
+ * With dropout_p > 0, dQ is accumulated with fp32 atomics, so its last bits
+ * may vary run to run. With dropout_p == 0 the call takes the two-pass form of
+ * fa_bwd_deterministic (faster there) and the result is bitwise deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
            void* stream);
+
+/*
+ * Backward pass, bf16, bitwise deterministic run to run: the same arguments,
+ * workspace contract and result definition as fa_bwd, but dQ comes from a
+ * second pass over the query blocks that recomputes P and dS (the dropout mask
+ * is regenerated a second time from the same Philox counters) and sums each
+ * dQ row's key tiles in a fixed order, instead of fp32 atomics. dK and dV are
+ * the same bits fa_bwd writes; without dropout so is dQ (fa_bwd takes this
+ * path then). (Dao, FlashAttention-2, section 3.1.2: the
+ * backward computes dQ from the same recomputed dS that gives dK and dV.)
+ */
+int fa_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, float scale, int causal,
+                         float dropout_p, uint64_t seed, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* The same two passes for fp32 tensors (fp32 arithmetic throughout). */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

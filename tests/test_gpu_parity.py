@@ -11,9 +11,11 @@ Two readings of those bounds, both forced by the output dtype:
   so no bf16 result could meet it. There the bound per element is
   half an ulp of O_ref plus 2^-9 |O_ref| (the rounding of P to bf16); below
   |O_ref| = 4 that expression is under 1e-2 and the plain bound applies.
-* A gradient whose reference is identically zero (one key, or a dropped
-  single key) has no "max"; it is measured relative to the largest reference
-  gradient of the same head, or absolutely if all three are zero.
+* A gradient whose reference is zero by the mathematics (one visible key, or
+  a dropped single key) has no "max": fp64 leaves it as rounding noise of
+  order 1e-17. Such a reference (max below 1e-9 of the head's largest
+  reference gradient) is measured relative to that largest gradient, or
+  absolutely if all three are zero.
 """
 import math
 
@@ -79,9 +81,15 @@ def o_bound(ref, tol, dtype):
 
 
 def rel_to_max(g, ref, fallback=None):
+    """max|g - ref| / max|ref|. A reference that the mathematics makes zero (one
+    visible key: dS, hence dQ and dK, vanish) leaves fp64 as rounding noise;
+    below 1e-9 of `fallback` (the head's largest reference gradient) the error
+    is taken relative to `fallback`, and absolutely if that is zero as well."""
     denom = np.abs(ref).max()
+    if fallback and denom < 1e-9 * fallback:
+        denom = fallback
     if denom == 0.0:
-        denom = fallback if fallback else 1.0
+        denom = 1.0
     return float(np.abs(g - ref).max() / denom)
 
 
