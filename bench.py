@@ -9,8 +9,10 @@ carries the forward+backward measurement on the dropout workload
 (B=2, H=16, N=4096, d=64, p=0.1; the backward in both its fused atomic form
 and its two-pass deterministic form), the backward at the default workload's
 shape, the decode-shaped forward on its three workloads (HBM-bound: GB/s
-against 8 TB/s), the roofline of the dominant kernel and the CPU oracle's
-throughput on a bounded sample.
+against 8 TB/s), the general entry points on head sizes 32/96/256, fp16,
+[B, N, H, d] storage and a packed variable-length batch (`coverage`), the
+roofline of the dominant kernel and the CPU oracle's throughput on a bounded
+sample.
 
 FLOPs are counted as 4*B*H*N^2*d for the forward, halved when causal, and
 2.5x that for the backward.
@@ -33,8 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "fwd_causal_q4_bf16_b2h32n8192d128"
 FWD_BWD_WORKLOAD = "fwdbwd_causal_dropout_bf16_b2h16n4096d64"
-FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp",
-               "exact_io_aware_53_amd/csrc/fa_tiles.hpp"]
+FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd.hip", "exact_io_aware_53_amd/csrc/fa_fwd_kernel.hpp",
+               "exact_io_aware_53_amd/csrc/fa_device.hpp", "exact_io_aware_53_amd/csrc/fa_tiles.hpp",
+               "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
 
 
 def source_hash(paths):
@@ -119,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-bwd", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-coverage", action="store_true",
+                    help="skip the head-size / fp16 / layout / packed-batch measurements")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (for HBM counter calibration)")
@@ -267,6 +272,45 @@ def main():
                                      "traffic": None, "ideal_io_bytes": wd.io_bytes()}})
             del td, od, ld, wsd
         line["decode"] = dec
+
+    if not args.no_coverage:
+        from exact_io_aware_53_amd.inputs import COVERAGE_WORKLOADS, make_coverage_inputs
+        cov = []
+        for wc in COVERAGE_WORKLOADS.values():
+            hc = make_coverage_inputs(wc)
+            t = {n: x.to(dev) for n, x in hc.items()}
+            del hc
+            if wc.layout == "varlen":
+                mx = int(wc.lengths().max())
+                o_c, l_c = fa.fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], mx, causal=wc.causal)
+
+                def fc():
+                    fa.fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], mx, causal=wc.causal,
+                                  out=o_c, lse=l_c)
+
+                def bc():
+                    fa.bwd_varlen(t["q"], t["k"], t["v"], o_c, l_c, t["do"], t["cu_seqlens"], mx,
+                                  causal=wc.causal)
+            else:
+                view = (lambda x: x.transpose(1, 2)) if wc.layout == "bshd" else (lambda x: x)
+                q_c, k_c, v_c, do_c = (view(t[n]) for n in ("q", "k", "v", "do"))
+                o_c, l_c = fa.fwd_ex(q_c, k_c, v_c, causal=wc.causal)
+
+                def fc():
+                    fa.fwd_ex(q_c, k_c, v_c, causal=wc.causal, out=o_c, lse=l_c)
+
+                def bc():
+                    fa.bwd_ex(q_c, k_c, v_c, o_c, l_c, do_c, causal=wc.causal)
+
+            _, evf = time_launches(fc, args.steps, args.warmup, stream)
+            _, evb = time_launches(bc, max(5, args.steps // 3), 2, stream)
+            mf, mb = sum(evf) / len(evf), sum(evb) / len(evb)
+            cov.append({"workload": wc.name, "ms_fwd": round(mf, 4), "ms_bwd": round(mb, 4),
+                        "tflops_fwd": round(wc.fwd_flops() / (mf * 1e-3) / 1e12, 3),
+                        "tflops_bwd": round(wc.bwd_flops() / (mb * 1e-3) / 1e12, 3)})
+            del t, o_c, l_c
+            torch.cuda.empty_cache()
+        line["coverage"] = cov
 
     if args.calibrate_copy:
         # A plain elementwise copy of known size: reads and writes 2^30 bytes per launch.

@@ -9,6 +9,9 @@ CPU or PyTorch fallback: if libfa.so is missing, every call raises.
     o, lse = fwd(q, k, v, causal=True)             # q, k, v: [B, H, N, d] bf16 or fp32 on the GPU
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
     o, lse = fwd_decode(q_new, k_cache, v_cache)   # [B, H, Nq, d] against [B, H, Nk, d], bf16
+    o, lse = fwd(q.transpose(1, 2), ...)           # any strided [B, H, N, d] view, bf16 or fp16,
+                                                   # d in {32, 64, 96, 128, 256}
+    o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen)   # packed [total, H, d] sequences
 """
 from __future__ import annotations
 
@@ -41,6 +44,29 @@ SIGNATURES = {
     "fa_dropout_mask": (_I, [_P, _I, _I, _I, _I, _I, _F, _U64, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
+
+
+
+class Layout(ctypes.Structure):
+    """fa_layout: element strides of a [B, H, N, d] view (d contiguous)."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    """fa_problem of include/fa.h."""
+    _fields_ = [("B", _I), ("H", _I), ("N", _I), ("d", _I), ("dtype", _I),
+                ("cu_seqlens", _P), ("total_tokens", _I),
+                ("q", Layout), ("k", Layout), ("v", Layout), ("o", Layout), ("lse", Layout),
+                ("dout", Layout), ("dq", Layout), ("dk", Layout), ("dv", Layout)]
+
+
+_PB = ctypes.POINTER(Problem)
+SIGNATURES.update({
+    "fa_fwd_ex": (_I, [_PB, _P, _P, _P, _P, _P, _F, _I, _F, _U64, _P]),
+    "fa_bwd_ex": (_I, [_PB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _F, _U64, _I, _P, _SZ, _P]),
+    "fa_bwd_ex_workspace_size": (_SZ, [_PB]),
+})
+FA_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
 
 _lib = None
 
@@ -105,6 +131,138 @@ def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out=None, lse=
                                    float(dropout_p), int(seed) & (2**64 - 1), _stream(q.device))
     _check(st, "fa_fwd")
     return out, lse
+
+
+def _layout4(t: torch.Tensor, name: str) -> Layout:
+    """Strides of a [B, H, N, d] view whose last dimension is contiguous."""
+    if t.dim() != 4 or not t.is_cuda:
+        raise ValueError(f"{name} must be a [B, H, N, d] GPU tensor")
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError(f"{name}: the d dimension must be contiguous")
+    return Layout(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _layout3(t: torch.Tensor, name: str) -> Layout:
+    """Strides of a packed [total, H, d] tensor (d contiguous); no batch stride."""
+    if t.dim() != 3 or not t.is_cuda:
+        raise ValueError(f"{name} must be a packed [total, H, d] GPU tensor")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError(f"{name}: the d dimension must be contiguous")
+    return Layout(0, t.stride(1), t.stride(0))
+
+
+def _problem(B, H, N, d, dtype, cu=None, total=0, **layouts) -> Problem:
+    if dtype not in FA_DTYPE:
+        raise ValueError("tensors must be bfloat16 or float16")
+    pb = Problem(B=B, H=H, N=N, d=d, dtype=FA_DTYPE[dtype],
+                 cu_seqlens=cu.data_ptr() if cu is not None else None, total_tokens=total)
+    for name, lay in layouts.items():
+        setattr(pb, name, lay)
+    return pb
+
+
+def fwd_ex(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out=None, lse=None):
+    """Forward pass on strided [B, H, N, d] views (bf16 or fp16, d in {32, 64, 96,
+    128, 256}), e.g. q.transpose(1, 2) of [B, N, H, d] storage. O gets q's strides
+    unless `out` is given; LSE is [B, H, N] fp32."""
+    B, H, N, d = q.shape
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must share the [B, H, N, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share the dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse.dim() != 3:
+        raise ValueError("lse must be [B, H, N]")
+    pb = _problem(B, H, N, d, q.dtype, q=_layout4(q, "q"), k=_layout4(k, "k"), v=_layout4(v, "v"),
+                  o=_layout4(out, "out"), lse=Layout(lse.stride(0), lse.stride(1), lse.stride(2)))
+    st = lib().fa_fwd_ex(ctypes.byref(pb), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), scale, int(bool(causal)), float(dropout_p),
+                         int(seed) & (2**64 - 1), _stream(q.device))
+    _check(st, "fa_fwd_ex")
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, causal=False, dropout_p=0.0, seed=0,
+               out=None, lse=None):
+    """Forward pass on packed sequences: q, k, v are [total, H, d] (bf16 or fp16),
+    sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32 on the GPU, B+1
+    entries), max_seqlen >= every length. Returns O [total, H, d] and LSE [H, total]."""
+    total, H, d = q.shape
+    if tuple(k.shape) != (total, H, d) or tuple(v.shape) != (total, H, d):
+        raise ValueError("q, k, v must share the [total, H, d] shape")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device) if lse is None else lse
+    pb = _problem(B, H, int(max_seqlen), d, q.dtype, cu=cu_seqlens, total=total,
+                  q=_layout3(q, "q"), k=_layout3(k, "k"), v=_layout3(v, "v"),
+                  o=_layout3(out, "out"), lse=Layout(0, lse.stride(0), lse.stride(1)))
+    st = lib().fa_fwd_ex(ctypes.byref(pb), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), scale, int(bool(causal)), float(dropout_p),
+                         int(seed) & (2**64 - 1), _stream(q.device))
+    _check(st, "fa_fwd_ex")
+    return out, lse
+
+
+def _bwd_ex_call(pb, q, k, v, o, lse, do, dq, dk, dv, scale, causal, dropout_p, seed, deterministic,
+                 workspace):
+    need = int(lib().fa_bwd_ex_workspace_size(ctypes.byref(pb)))
+    if need == 0:
+        raise FAError(FA_ERR_INVALID_ARG, "fa_bwd_ex_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd_ex(ctypes.byref(pb), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         scale, int(bool(causal)), float(dropout_p), int(seed) & (2**64 - 1),
+                         int(bool(deterministic)), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "fa_bwd_ex")
+
+
+def bwd_ex(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0, dq=None, dk=None,
+           dv=None, workspace=None, deterministic=False):
+    """Backward of fwd_ex on strided [B, H, N, d] views (bf16 or fp16). Gradients
+    take the strides of q, k, v unless given."""
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, do must share the [B, H, N, d] shape and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    pb = _problem(B, H, N, d, q.dtype, q=_layout4(q, "q"), k=_layout4(k, "k"), v=_layout4(v, "v"),
+                  o=_layout4(o, "o"), lse=Layout(lse.stride(0), lse.stride(1), lse.stride(2)),
+                  dout=_layout4(do, "do"), dq=_layout4(dq, "dq"), dk=_layout4(dk, "dk"),
+                  dv=_layout4(dv, "dv"))
+    _bwd_ex_call(pb, q, k, v, o, lse, do, dq, dk, dv, scale, causal, dropout_p, seed, deterministic,
+                 workspace)
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, scale=None, causal=False, dropout_p=0.0,
+               seed=0, dq=None, dk=None, dv=None, workspace=None, deterministic=False):
+    """Backward of fwd_varlen: packed [total, H, d] tensors, LSE [H, total]."""
+    total, H, d = q.shape
+    for t in (k, v, o, do):
+        if tuple(t.shape) != (total, H, d) or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, do must share the [total, H, d] shape and dtype")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    pb = _problem(B, H, int(max_seqlen), d, q.dtype, cu=cu_seqlens, total=total,
+                  q=_layout3(q, "q"), k=_layout3(k, "k"), v=_layout3(v, "v"), o=_layout3(o, "o"),
+                  lse=Layout(0, lse.stride(0), lse.stride(1)), dout=_layout3(do, "do"),
+                  dq=_layout3(dq, "dq"), dk=_layout3(dk, "dk"), dv=_layout3(dv, "dv"))
+    _bwd_ex_call(pb, q, k, v, o, lse, do, dq, dk, dv, scale, causal, dropout_p, seed, deterministic,
+                 workspace)
+    return dq, dk, dv
 
 
 def workspace_size(B: int, H: int, N: int, d: int) -> int:

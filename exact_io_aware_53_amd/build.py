@@ -40,9 +40,18 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+def flags(src: str):
+    """Compile flags of one source. Kernels of head size 256 (*_d256.hip) hold
+    more than 256 registers per lane, so they let matrix-core accumulators live
+    in the AGPR half of the register file."""
+    if src.endswith("_d256.hip"):
+        return [f for f in COMMON if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=1")]
+    return COMMON
+
+
 def _compile(src: str, defines=(), build_dir=BUILD) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *COMMON, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *flags(src), *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

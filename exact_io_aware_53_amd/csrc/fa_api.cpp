@@ -27,6 +27,9 @@ int check_shape(int B, int H, int N, int d, float scale, float dropout_p) {
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;   // also rejects NaN
     if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;   // also rejects NaN
     if ((long long)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    // a head's rows, ragged tail tiles included, within 32-bit offsets below the
+    // out-of-range offset of zero-filled chunks (0xf0000000)
+    if ((long long)(N + 256) * d * 4 >= 0xf0000000LL) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
@@ -65,8 +68,56 @@ int fwd_common(bool bf16, const void* q, const void* k, const void* v, void* o, 
     const int st = check_shape(B, H, N, d, scale, dropout_p);
     if (st != FA_OK) return st;
     fa::FwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, lse};
+    a.L = fa::contiguous_layouts(H, N, d);
     hipStream_t s = (hipStream_t)stream;
-    return map_hip(bf16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+    return map_hip(bf16 ? fa::launch_fwd_mfma(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+bool head_size_ok(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
+
+// Bytes a head's rows may span: below the out-of-range offset (0xf0000000)
+// the kernels use for zero-filled chunks.
+constexpr long long kHeadBytes = 0xf0000000LL;
+
+// One 16-bit tensor's strides: non-negative, 16-byte aligned rows, rows not
+// overlapping, and rows 0 .. N+255 of a head within kHeadBytes.
+bool strides16_ok(const fa_layout& l, int N, int d, fa::Strides& out) {
+    if (l.batch < 0 || l.head < 0 || l.row < d) return false;
+    if (l.batch % 8 != 0 || l.head % 8 != 0 || l.row % 8 != 0) return false;
+    if ((long long)(N + 256) * l.row * 2 >= kHeadBytes) return false;
+    out = fa::Strides{l.batch, l.head, (int)l.row};
+    return true;
+}
+
+bool strides32_ok(const fa_layout& l, int N, fa::Strides& out) {
+    if (l.batch < 0 || l.head < 0 || l.row < 1) return false;
+    if ((long long)(N + 256) * l.row * 4 >= kHeadBytes) return false;
+    out = fa::Strides{l.batch, l.head, (int)l.row};
+    return true;
+}
+
+// Validates a problem description and turns it into kernel layouts.
+int problem_layouts(const fa_problem* pb, bool backward, fa::TensorLayouts& L) {
+    if (!pb) return FA_ERR_INVALID_ARG;
+    if (pb->B < 1 || pb->H < 1 || pb->N < 1 || pb->d < 1) return FA_ERR_INVALID_ARG;
+    if (!head_size_ok(pb->d)) return FA_ERR_UNSUPPORTED;
+    if (pb->dtype != FA_DTYPE_BF16 && pb->dtype != FA_DTYPE_FP16) return FA_ERR_UNSUPPORTED;
+    const int N = pb->N, d = pb->d;
+    if (!strides16_ok(pb->q, N, d, L.q) || !strides16_ok(pb->k, N, d, L.k) ||
+        !strides16_ok(pb->v, N, d, L.v) || !strides16_ok(pb->o, N, d, L.o) ||
+        !strides32_ok(pb->lse, N, L.lse))
+        return FA_ERR_INVALID_ARG;
+    if (backward && (!strides16_ok(pb->dout, N, d, L.dout) || !strides16_ok(pb->dq, N, d, L.dq) ||
+                     !strides16_ok(pb->dk, N, d, L.dk) || !strides16_ok(pb->dv, N, d, L.dv)))
+        return FA_ERR_INVALID_ARG;
+    if ((long long)pb->B * pb->H * ((N + 255) / 256) > (1LL << 30)) return FA_ERR_INVALID_ARG;
+    L.cu_seqlens = pb->cu_seqlens;
+    L.total = 0;
+    if (pb->cu_seqlens) {
+        if (((uintptr_t)pb->cu_seqlens & 3u) != 0 || pb->total_tokens < 1) return FA_ERR_INVALID_ARG;
+        L.total = pb->total_tokens;
+    }
+    return FA_OK;
 }
 
 int bwd_common(bool bf16, const void* q, const void* k, const void* v, const void* o,
@@ -89,8 +140,9 @@ int bwd_common(bool bf16, const void* q, const void* k, const void* v, const voi
     float* lse2 = (float*)((char*)dsum + round256(rows * sizeof(float)));
     fa::BwdArgs a{shape(B, H, N, d, scale, causal, dropout_p, seed), q, k, v, o, dout, lse,
                   dq, dk, dv, dq_acc, dsum, lse2, deterministic};
+    a.L = fa::contiguous_layouts(H, N, d);
     hipStream_t s = (hipStream_t)stream;
-    return map_hip(bf16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
+    return map_hip(bf16 ? fa::launch_bwd_mfma(a, s) : fa::launch_bwd_f32(a, s));
 }
 
 }  // namespace
@@ -205,6 +257,60 @@ size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
     return decode_workspace_bytes(B, H, Nq, Nk, d);
 }
 
+int fa_fwd_ex(const fa_problem* pb, const void* q, const void* k, const void* v, void* o,
+              float* lse, float scale, int causal, float dropout_p, uint64_t seed, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) != 0)
+        return FA_ERR_INVALID_ARG;
+    fa::TensorLayouts L;
+    const int st = problem_layouts(pb, false, L);
+    if (st != FA_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a{shape(pb->B, pb->H, pb->N, pb->d, scale, causal, dropout_p, seed), q, k, v, o, lse};
+    a.L = L;
+    a.fp16 = pb->dtype == FA_DTYPE_FP16;
+    return map_hip(fa::launch_fwd_mfma(a, (hipStream_t)stream));
+}
+
+// Width the backward computes at: head sizes 32 and 96 run on rows padded to 64 and 128.
+int compute_width(int d) { return d == 32 ? 64 : d == 96 ? 128 : d; }
+
+size_t fa_bwd_ex_workspace_size(const fa_problem* pb) {
+    fa::TensorLayouts L;
+    if (problem_layouts(pb, true, L) != FA_OK) return 0;
+    return workspace_bytes(pb->B, pb->H, pb->N, compute_width(pb->d));
+}
+
+int fa_bwd_ex(const fa_problem* pb, const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* dk, void* dv, float scale,
+              int causal, float dropout_p, uint64_t seed, int deterministic, void* workspace,
+              size_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)lse & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
+    fa::TensorLayouts L;
+    const int st = problem_layouts(pb, true, L);
+    if (st != FA_OK) return st;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;
+    const int B = pb->B, H = pb->H, N = pb->N, dc = compute_width(pb->d);
+    if ((long long)B * H * N * dc > kMaxElems) return FA_ERR_INVALID_ARG;   // workspace indexing
+    if (ws_bytes < workspace_bytes(B, H, N, dc)) return FA_ERR_INVALID_ARG;
+    const size_t rows = (size_t)B * H * N;
+    float* dq_acc = (float*)workspace;
+    float* dsum = (float*)((char*)workspace + round256(rows * dc * sizeof(float)));
+    float* lse2 = (float*)((char*)dsum + round256(rows * sizeof(float)));
+    fa::BwdArgs a{shape(B, H, N, pb->d, scale, causal, dropout_p, seed), q, k, v, o, dout, lse,
+                  dq, dk, dv, dq_acc, dsum, lse2, deterministic != 0};
+    a.L = L;
+    a.fp16 = pb->dtype == FA_DTYPE_FP16;
+    return map_hip(fa::launch_bwd_mfma(a, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
     if ((long long)B * H * N * d > kMaxElems) return 0;
@@ -225,7 +331,7 @@ const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head size";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head size or dtype";
         case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch error";
         default: return "unknown fa_status";
     }

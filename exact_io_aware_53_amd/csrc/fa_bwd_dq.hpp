@@ -1,5 +1,7 @@
 // dQ of the backward pass as a pass of its own, without atomics: the
 // deterministic variant (no fp32 accumulator in HBM, dQ written once).
+// Element types, layouts, packed sequences and padded head sizes as in the
+// key-side kernel (fa_bwd_kernels.hpp).
 //
 // Same gradient as the fused backward ("DL0056 FlashAttention", point (3);
 // inferensys glossary "FlashAttention", paragraph on recomputation): for each
@@ -21,6 +23,8 @@
 // ds_read_b64_tr_b16 (the A operand of dQ^T = K^T dS^T); dS^T, rounded to
 // bf16, is the B operand straight from registers. Causal query blocks are
 // paired long-with-short per workgroup, as in the forward.
+#pragma once
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -28,48 +32,61 @@ namespace fa {
 namespace {
 
 struct DqParams {
-    const __bf16* q;
-    const __bf16* k;
-    const __bf16* v;
-    const __bf16* dout;
-    const float* lse2;     // LSE * log2(e), [B,H,N]
-    const float* dsum;     // D_i, [B,H,N]
-    __bf16* dq;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse2;     // LSE * log2(e), [B*H, N] workspace rows
+    const float* dsum;     // D_i, [B*H, N] workspace rows
+    void* dq;
+    Strides lq, lk, lv, ldo, ldq;
+    const int* cu;
+    int total;
     int H, N, nqb, heads;
     float scale, sl2, inv_keep;
     uint32_t thr;
     PhiloxKey key;
 };
 
-// HBM -> LDS copy of a swizzled [BC x D] tile: 1 KB blocks shared by NW waves,
-// per-lane source offsets computed once; a tile adds t * BC rows.
-template <int D, int BC, int NW>
+// HBM -> LDS copy of a swizzled [BC x D] tile of a tensor with row stride ld
+// whose rows hold DH <= D elements (chunks past DH load as zeros): 1 KB blocks
+// shared by NW waves, per-lane source offsets computed once; a tile adds t * BC
+// rows.
+template <int D, int DH, int BC, int NW>
 struct SwizzledCopy {
     static constexpr int CH = D / 8, BLKS = BC * CH / 64, PER = (BLKS + NW - 1) / NW;
     static_assert(BLKS * 64 == BC * CH, "a tile is whole 1 KB copy blocks");
     uint32_t off[PER];
+    uint32_t step;
 
-    __device__ __forceinline__ SwizzledCopy(int wave, int lane) {
+    __device__ __forceinline__ SwizzledCopy(int wave, int lane, int ld) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int pos = (i * NW + wave) * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
-            off[i] = (uint32_t)(row * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2;
+            const int ch = sw ^ chunk_swizzle<CH>(row);
+            off[i] = ch * 8 < DH ? (uint32_t)(row * ld + ch * 8) * 2 : 0xf0000000u;
         }
+        step = (uint32_t)(BC * ld * 2);
     }
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, FA_LDS char* base, int t, int wave) const {
-        const uint32_t toff = __builtin_amdgcn_readfirstlane((uint32_t)t * (BC * D * 2));
+        const uint32_t toff = __builtin_amdgcn_readfirstlane((uint32_t)t * step);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int blk = i * NW + wave;
-            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), off[i] + toff);
+            // Padded chunks keep their out-of-range offset (no tile offset added,
+            // so it cannot wrap back into range).
+            const uint32_t o = DH == D || off[i] != 0xf0000000u ? off[i] + toff : off[i];
+            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), o);
         }
     }
 };
 
-template <int D, int BC, int NW, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, int DH, int BC, int NW, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void bwd_dq_kernel(DqParams p) {
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
     constexpr int BR = NW * 32;
     constexpr int CH = D / 8, ROW = D * 2;
     constexpr int KB = BC / 32, NC = BC / 16, DB = D / 32, NCD = D / 16;
@@ -93,18 +110,27 @@ void bwd_dq_kernel(DqParams p) {
         bh = blockIdx.x % p.heads;
         slot = blockIdx.x / p.heads;
     }
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    slot = __builtin_amdgcn_readfirstlane(slot);
     const int b = bh / p.H, h = bh - b * p.H;
-    const int N = p.N;
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const auto rs_q = make_rsrc(p.q + head, head_bytes);
-    const auto rs_k = make_rsrc(p.k + head, head_bytes);
-    const auto rs_v = make_rsrc(p.v + head, head_bytes);
-    const auto rs_do = make_rsrc(p.dout + head, head_bytes);
-    const auto rs_l = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4);
-    const auto rs_d = make_rsrc(p.dsum + (size_t)bh * N, (uint32_t)N * 4);
+    int start, N;
+    sequence(p.cu, p.total, p.N, b, start, N);
+    const int nqb = (N + BR - 1) / BR;
+    if (slot >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;    // past this sequence's blocks
+    const int ldq = p.lq.sn, ldo = p.ldo.sn;
+    const auto rs_q = make_rsrc((const T*)p.q + p.lq.base(b, h, start), (uint32_t)(((size_t)(N - 1) * ldq + DH) * 2));
+    const auto rs_k = make_rsrc((const T*)p.k + p.lk.base(b, h, start),
+                                (uint32_t)(((size_t)(N - 1) * p.lk.sn + DH) * 2));
+    const auto rs_v = make_rsrc((const T*)p.v + p.lv.base(b, h, start),
+                                (uint32_t)(((size_t)(N - 1) * p.lv.sn + DH) * 2));
+    const auto rs_do = make_rsrc((const T*)p.dout + p.ldo.base(b, h, start),
+                                 (uint32_t)(((size_t)(N - 1) * ldo + DH) * 2));
+    const size_t wrow = (size_t)bh * p.N;
+    const auto rs_l = make_rsrc(p.lse2 + wrow, (uint32_t)N * 4);
+    const auto rs_d = make_rsrc(p.dsum + wrow, (uint32_t)N * 4);
 
-    const SwizzledCopy<D, BC, NW> copy(wave, lane);
+    const SwizzledCopy<D, DH, BC, NW> kcopy(wave, lane, p.lk.sn);
+    const SwizzledCopy<D, DH, BC, NW> vcopy(wave, lane, p.lv.sn);
     // Row operand (K for S^T, V for dP^T): key row 32kb + l32, d = 16c + 8hi .. +7.
     int roff[NCD];
 #pragma unroll
@@ -127,12 +153,14 @@ void bwd_dq_kernel(DqParams p) {
         const int qw = q0 + wave * 32;
         const int my_q = qw + l32;
 
-        bf16x8 qreg[NCD], doreg[NCD];
+        V8 qreg[NCD], doreg[NCD];
 #pragma unroll
         for (int c = 0; c < NCD; ++c) {
-            const uint32_t o = (uint32_t)(my_q * D + 16 * c + 8 * hi) * 2;
-            qreg[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_q, o));
-            doreg[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_do, o));
+            const bool live = 16 * c + 8 * hi < DH;    // padded columns load as zeros
+            qreg[c] = __builtin_bit_cast(V8, buffer_load16(rs_q, live ? (uint32_t)(my_q * ldq + 16 * c + 8 * hi) * 2
+                                                                    : 0xf0000000u));
+            doreg[c] = __builtin_bit_cast(V8, buffer_load16(rs_do, live ? (uint32_t)(my_q * ldo + 16 * c + 8 * hi) * 2
+                                                                      : 0xf0000000u));
         }
         const float lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_l, (uint32_t)my_q * 4, 0, 0));
         const float dsum = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_d, (uint32_t)my_q * 4, 0, 0));
@@ -145,19 +173,19 @@ void bwd_dq_kernel(DqParams p) {
             for (int r = 0; r < 16; ++r) dqa[i][r] = 0.0f;
 
         const int last_q = min(N, q0 + BR) - 1;
-        const int T = CAUSAL ? last_q / BC + 1 : (N + BC - 1) / BC;
-        const int Tw = qw >= N ? 0 : CAUSAL ? min(T, min(qw + 31, N - 1) / BC + 1) : T;
+        const int nt = CAUSAL ? last_q / BC + 1 : (N + BC - 1) / BC;
+        const int Tw = qw >= N ? 0 : CAUSAL ? min(nt, min(qw + 31, N - 1) / BC + 1) : nt;
 
         auto issue = [&](int t, int buf) {
-            copy.issue(rs_k, (FA_LDS char*)kbuf + buf * TILE, t, wave);
-            copy.issue(rs_v, (FA_LDS char*)vbuf + buf * TILE, t, wave);
+            kcopy.issue(rs_k, (FA_LDS char*)kbuf + buf * TILE, t, wave);
+            vcopy.issue(rs_v, (FA_LDS char*)vbuf + buf * TILE, t, wave);
         };
         issue(0, 0);
-        for (int t = 0; t < T; ++t) {
+        for (int t = 0; t < nt; ++t) {
             const int buf = t & 1;
             wait_vmem();
             __syncthreads();
-            if (t + 1 < T) issue(t + 1, buf ^ 1);
+            if (t + 1 < nt) issue(t + 1, buf ^ 1);
             if (t >= Tw) continue;
             const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * TILE;
             const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * TILE;
@@ -170,10 +198,8 @@ void bwd_dq_kernel(DqParams p) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const int o = roff[c] + kb * 32 * ROW;
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const FA_LDS bf16x8*)(kt + o), qreg[c],
-                                                                    c == 0 ? f32x16{} : s[kb], 0, 0, 0);
-                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const FA_LDS bf16x8*)(vt + o), doreg[c],
-                                                                     c == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+                    s[kb] = mfma32(*(const FA_LDS V8*)(kt + o), qreg[c], c == 0 ? f32x16{} : s[kb]);
+                    dp[kb] = mfma32(*(const FA_LDS V8*)(vt + o), doreg[c], c == 0 ? f32x16{} : dp[kb]);
                 }
             // log2 P = s * scale * log2(e) - LSE_i * log2(e); masked elements -> -inf
 #pragma unroll
@@ -188,7 +214,7 @@ void bwd_dq_kernel(DqParams p) {
                     for (int r = 0; r < 16; ++r)
                         s[kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[kb][r];
             }
-            bf16x8 dsb[NC];
+            V8 dsb[NC];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -205,44 +231,42 @@ void bwd_dq_kernel(DqParams p) {
                         ds[e] = pr * fmaf(dp[kb][r + e], z, -dsum);
                     }
                     const int pc = kb * 2 + r / 8, pi = r % 8;
-                    dsb[pc][pi] = (__bf16)ds[0];
-                    dsb[pc][pi + 1] = (__bf16)ds[1];
+                    dsb[pc][pi] = (T)ds[0];
+                    dsb[pc][pi + 1] = (T)ds[1];
                 }
             // dQ^T += K^T dS^T over the tile's 16-key chunks
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (FA_LDS s16x4*)(kt + troff[db][0] + 16 * c * ROW)));
-                    const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (FA_LDS s16x4*)(kt + troff[db][1] + 16 * c * ROW)));
-                    bf16x8 a;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        a[e] = x0[e];
-                        a[4 + e] = x1[e];
-                    }
-                    dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[c], dqa[db], 0, 0, 0);
+                    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (FA_LDS s16x4*)(kt + troff[db][0] + 16 * c * ROW));
+                    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (FA_LDS s16x4*)(kt + troff[db][1] + 16 * c * ROW));
+                    typedef short s16x8 __attribute__((ext_vector_type(8)));
+                    const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    dqa[db] = mfma32(a, dsb[c], dqa[db]);
                 }
         }
 
         if (my_q < N) {
-            __bf16* row = p.dq + head + (size_t)my_q * D;
+            T* row = (T*)p.dq + p.ldq.base(b, h, start) + (size_t)my_q * p.ldq.sn;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db) {
+                if (32 * db >= DH) break;          // padded columns are not stored
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    bf16x4 w;
+                    V4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = (__bf16)(dqa[db][4 * g + i] * p.scale);
-                    *(bf16x4*)(row + 32 * db + 8 * g + 4 * hi) = w;
+                    for (int i = 0; i < 4; ++i) w[i] = (T)(dqa[db][4 * g + i] * p.scale);
+                    *(V4*)(row + 32 * db + 8 * g + 4 * hi) = w;
                 }
+            }
         }
     };
 
     if (CAUSAL) {
-        const int longer = p.nqb - 1 - slot;
+        const int longer = nqb - 1 - slot;
         run_block(longer);
         if (slot != longer) {
             __syncthreads();     // every wave is done with the buffers the next block refills
@@ -253,17 +277,24 @@ void bwd_dq_kernel(DqParams p) {
     }
 }
 
-template <int D, bool CAUSAL, bool DROPOUT>
-hipError_t launch(const BwdArgs& a, hipStream_t st) {
+template <typename T, int D, int DH, bool CAUSAL, bool DROPOUT>
+hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t st) {
     constexpr int BC = 64, NW = 4, BR = NW * 32;
     DqParams p{};
-    p.q = (const __bf16*)a.q;
-    p.k = (const __bf16*)a.k;
-    p.v = (const __bf16*)a.v;
-    p.dout = (const __bf16*)a.dout;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
     p.lse2 = a.lse2;
     p.dsum = a.dsum;
-    p.dq = (__bf16*)a.dq;
+    p.dq = a.dq;
+    p.lq = a.L.q;
+    p.lk = a.L.k;
+    p.lv = a.L.v;
+    p.ldo = a.L.dout;
+    p.ldq = a.L.dq;
+    p.cu = a.L.cu_seqlens;
+    p.total = a.L.total;
     p.H = a.s.H;
     p.N = a.s.N;
     p.nqb = (a.s.N + BR - 1) / BR;
@@ -274,21 +305,18 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
     const int blocks = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, NW, CAUSAL, DROPOUT>), dim3(p.heads * blocks), dim3(NW * 64), 0, st,
-                       p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, DH, BC, NW, CAUSAL, DROPOUT>), dim3(p.heads * blocks), dim3(NW * 64),
+                       0, st, p);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a, hipStream_t st) {
+// The query-side pass of the two-pass backward: dQ only.
+template <typename T, int D, int DH>
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
-    if (a.s.d == 64) {
-        if (a.s.causal) return drop ? launch<64, true, true>(a, st) : launch<64, true, false>(a, st);
-        return drop ? launch<64, false, true>(a, st) : launch<64, false, false>(a, st);
-    }
-    if (a.s.causal) return drop ? launch<128, true, true>(a, st) : launch<128, true, false>(a, st);
-    return drop ? launch<128, false, true>(a, st) : launch<128, false, false>(a, st);
+    if (a.s.causal) return drop ? launch_dq_cfg<T, D, DH, true, true>(a, st) : launch_dq_cfg<T, D, DH, true, false>(a, st);
+    return drop ? launch_dq_cfg<T, D, DH, false, true>(a, st) : launch_dq_cfg<T, D, DH, false, false>(a, st);
 }
 
+}  // namespace
 }  // namespace fa

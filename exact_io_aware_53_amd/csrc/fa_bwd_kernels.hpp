@@ -1,4 +1,4 @@
-// Backward attention for bf16 tensors on gfx950 matrix cores.
+// Backward attention for bf16 and fp16 tensors on gfx950 matrix cores.
 //
 // Recomputation instead of storage (inferensys glossary "FlashAttention",
 // paragraph on recomputation; emergent.sh glossary "Flash Attention", "How
@@ -34,6 +34,13 @@
 // * Two-pass form (DQ = false): the same kernel without the dQ products, then
 //   bwd_dq_kernel for dQ. No atomics, so bitwise deterministic; without
 //   dropout it is also the faster form and the default.
+// * Layouts as in the forward: per-tensor batch/head/row strides, packed
+//   variable-length sequences. Head sizes 32 and 96 run the kernels of 64 and
+//   128 on rows padded with zeros (DH = the stored width, D = the computed
+//   one): padded columns load as zeros and are never stored.
+#pragma once
+
+#include "fa_bwd_dq.hpp"
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -43,43 +50,50 @@ namespace {
 constexpr int kBKV = 128;     // keys per workgroup
 constexpr int kNW = 4;        // waves per workgroup (32 keys each)
 
-struct BwdParamsB {
-    const __bf16* q;
-    const __bf16* k;
-    const __bf16* v;
-    const __bf16* dout;
-    const float* lse2;     // LSE_i * log2(e), written by the pre-pass
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse2;     // LSE_i * log2(e), written by the pre-pass ([B*H, N] rows)
     const float* dsum;
-    float* dq_acc;
-    __bf16* dk;
-    __bf16* dv;
+    float* dq_acc;         // [B*H, N, D] fp32
+    void* dk;
+    void* dv;
+    Strides lq, lk, lv, ldo, ldk, ldv;
+    const int* cu;         // packed sequences, or null
+    int total;
     int H, N, nkb, heads;
     float scale, sl2, inv_keep;
     uint32_t thr;
     PhiloxKey key;
 };
 
+// Source offset (bytes) of 16-byte chunk `ch` of row `row` in a tensor with
+// row stride ld whose stored rows are DH elements wide; chunks past DH come
+// from an out-of-range offset and load as zeros.
+template <int DH>
+__device__ __forceinline__ uint32_t chunk_src(int row, int ch, int ld) {
+    return ch * 8 < DH ? (uint32_t)(row * ld + ch * 8) * 2 : 0xf0000000u;
+}
+
 // Transposed matrix-core operand: two ds_read_b64_tr_b16 at per-lane byte
 // offsets off0/off1 (the first and second 8 rows of a 16-row block).
-__device__ __forceinline__ bf16x8 tr_read(const FA_LDS char* base, int off0, int off1) {
-    const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                   (FA_LDS s16x4*)(base + off0)));
-    const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                   (FA_LDS s16x4*)(base + off1)));
-    bf16x8 a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = x0[i];
-        a[4 + i] = x1[i];
-    }
-    return a;
+template <typename V8>
+__device__ __forceinline__ V8 tr_read(const FA_LDS char* base, int off0, int off1) {
+    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off0));
+    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // DQ = false: the key/value side only (dK, dV); dQ then comes from its own
 // pass (bwd_dq_kernel). Without the dQ products the Q/dO tiles are
 // double-buffered and one barrier per tile remains.
-template <int D, int BQ, bool CAUSAL, bool DROPOUT, bool DQ>
-__global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
+template <typename T, int D, int DH, int BQ, bool CAUSAL, bool DROPOUT, bool DQ>
+__global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
     constexpr int CH = D / 8;
     constexpr int QB = BQ / 32;        // 32-row query blocks per tile
     constexpr int DB = D / 32;
@@ -91,7 +105,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     static_assert(BQ == 64, "dS^T rows need 8 chunks for the swizzle");
     static_assert((QB * DB) % kNW == 0, "dQ blocks must split evenly over the waves");
     constexpr int DQ_ATOMICS = (QB * DB / kNW) * 16;   // dQ atomics per lane per tile
-    static_assert(DQ_ATOMICS <= 63, "vmcnt holds at most 63");
+    static_assert(!DQ || DQ_ATOMICS <= 63, "vmcnt holds at most 63");
 
     constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
     __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
@@ -123,19 +137,26 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     bh = __builtin_amdgcn_readfirstlane(bh);
     kb = __builtin_amdgcn_readfirstlane(kb);
     const int b = bh / p.H, h = bh - b * p.H;
-    const int N = p.N;
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const auto rs_q = make_rsrc(p.q + head, head_bytes);
-    const auto rs_k = make_rsrc(p.k + head, head_bytes);
-    const auto rs_v = make_rsrc(p.v + head, head_bytes);
-    const auto rs_do = make_rsrc(p.dout + head, head_bytes);
-    const auto rs_lse = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4);
-    const auto rs_ds = make_rsrc(p.dsum + (size_t)bh * N, (uint32_t)N * 4);
-    // dQ accumulator of the head; atomics at rows >= N fall outside and are dropped.
-    const auto rs_dq = make_rsrc(p.dq_acc + head, (uint32_t)N * D * 4);
-
+    int start, N;
+    sequence(p.cu, p.total, p.N, b, start, N);
     const int j0 = kb * kBKV;
+    if (j0 >= N) return;                          // past this sequence's keys
+    const int ldq = p.lq.sn, ldk = p.lk.sn, ldv = p.lv.sn, ldo = p.ldo.sn;
+    const T* const qh = (const T*)p.q + p.lq.base(b, h, start);
+    const T* const kh = (const T*)p.k + p.lk.base(b, h, start);
+    const T* const vh = (const T*)p.v + p.lv.base(b, h, start);
+    const T* const doh = (const T*)p.dout + p.ldo.base(b, h, start);
+    const auto rs_q = make_rsrc(qh, (uint32_t)(((size_t)(N - 1) * ldq + DH) * 2));
+    const auto rs_k = make_rsrc(kh, (uint32_t)(((size_t)(N - 1) * ldk + DH) * 2));
+    const auto rs_v = make_rsrc(vh, (uint32_t)(((size_t)(N - 1) * ldv + DH) * 2));
+    const auto rs_do = make_rsrc(doh, (uint32_t)(((size_t)(N - 1) * ldo + DH) * 2));
+    // Row terms and the dQ accumulator: [B*H, p.N] rows in the workspace.
+    const size_t wrow = (size_t)bh * p.N;
+    const auto rs_lse = make_rsrc(p.lse2 + wrow, (uint32_t)N * 4);
+    const auto rs_ds = make_rsrc(p.dsum + wrow, (uint32_t)N * 4);
+    // dQ accumulator of the head; atomics at rows >= N fall outside and are dropped.
+    const auto rs_dq = make_rsrc(p.dq_acc + wrow * D, (uint32_t)N * D * 4);
+
     const int kw = j0 + wave * 32;     // first key of this wave
     const int my_key = kw + l32;
 
@@ -162,12 +183,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
     constexpr int ROW = D * 2, SROW = BQ * 2;     // LDS row bytes: Q/dO/K tiles, dS^T tile
 
     // K and V rows of this wave's keys as B operands (d chunk c: d = 16c + 8hi .. +7)
-    bf16x8 kt[NCD], vt[NCD];
+    V8 kt[NCD], vt[NCD];
 #pragma unroll
     for (int c = 0; c < NCD; ++c) {
-        const uint32_t off = (uint32_t)(my_key * D + 16 * c + 8 * hi) * 2;
-        kt[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_k, off));
-        vt[c] = __builtin_bit_cast(bf16x8, buffer_load16(rs_v, off));
+        kt[c] = __builtin_bit_cast(V8, buffer_load16(rs_k, chunk_src<DH>(my_key, 2 * c + hi, ldk)));
+        vt[c] = __builtin_bit_cast(V8, buffer_load16(rs_v, chunk_src<DH>(my_key, 2 * c + hi, ldv)));
     }
     // All 128 keys of the block into LDS for the dQ products.
     if (DQ) {
@@ -176,7 +196,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
             buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
-                            (uint32_t)((j0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2);
+                            chunk_src<DH>(j0 + row, sw ^ chunk_swizzle<CH>(row), ldk));
         }
     }
 
@@ -191,9 +211,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
         for (int i = 0; i < QLOADS; ++i) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
-            const uint32_t off = (uint32_t)((i0 + row) * D + ((sw ^ chunk_swizzle<CH>(row)) << 3)) * 2;
-            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + buf * TILE + blk * 1024), off);
-            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), off);
+            const int ch = sw ^ chunk_swizzle<CH>(row);
+            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldq));
+            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldo));
         }
         if (wave == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)(lse_s + buf * BQ), 4,
@@ -247,10 +267,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
                 for (int c = 0; c < NCD; ++c) {
                     const int o = roff[c] + qb * 32 * ROW;
-                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *(const FA_LDS bf16x8*)(qT + o), kt[c], s[qb], 0, 0, 0);
-                    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *(const FA_LDS bf16x8*)(doT + o), vt[c], dp[qb], 0, 0, 0);
+                    s[qb] = mfma32(*(const FA_LDS V8*)(qT + o), kt[c], s[qb]);
+                    dp[qb] = mfma32(*(const FA_LDS V8*)(doT + o), vt[c], dp[qb]);
                 }
             }
             // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
@@ -293,19 +311,17 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
             // dV^T += dO^T (P Z'),  dK^T += Q^T dS  (contraction over the tile's query rows)
 #pragma unroll
             for (int qc = 0; qc < BQ / 16; ++qc) {
-                bf16x8 bp, bs;
+                V8 bp, bs;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    bp[i] = (__bf16)s[qc >> 1][8 * (qc & 1) + i];
-                    bs[i] = (__bf16)dp[qc >> 1][8 * (qc & 1) + i];
+                    bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
+                    bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
-                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(doT, o0, o1), bp,
-                                                                     dva[db], 0, 0, 0);
-                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qT, o0, o1), bs,
-                                                                     dka[db], 0, 0, 0);
+                    dva[db] = mfma32(tr_read<V8>(doT, o0, o1), bp, dva[db]);
+                    dka[db] = mfma32(tr_read<V8>(qT, o0, o1), bs, dka[db]);
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
@@ -315,8 +331,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     u32x2 w;
-                    w[0] = pack_bf16x2(dp[qb][4 * g + 0], dp[qb][4 * g + 1]);
-                    w[1] = pack_bf16x2(dp[qb][4 * g + 2], dp[qb][4 * g + 3]);
+                    w[0] = pack2<T>(dp[qb][4 * g + 0], dp[qb][4 * g + 1]);
+                    w[1] = pack2<T>(dp[qb][4 * g + 2], dp[qb][4 * g + 3]);
                     *(FA_LDS u32x2*)(dsL + tile_offset<BQ / 8>(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi)) = w;
                 }
         }
@@ -333,10 +349,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
             for (int kc = 0; kc < kBKV / 16; ++kc)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    tr_read(dsL, tsoff[qb][0] + 16 * kc * SROW, tsoff[qb][1] + 16 * kc * SROW),
-                    tr_read(kL, troff[db][0] + 16 * kc * ROW, troff[db][1] + 16 * kc * ROW), acc,
-                    0, 0, 0);
+                acc = mfma32(tr_read<V8>(dsL, tsoff[qb][0] + 16 * kc * SROW, tsoff[qb][1] + 16 * kc * SROW),
+                             tr_read<V8>(kL, troff[db][0] + 16 * kc * ROW, troff[db][1] + 16 * kc * ROW), acc);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qi = i0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -348,84 +362,136 @@ __global__ __launch_bounds__(kNW * 64) void bwd_bf16_kernel(BwdParamsB p) {
 
     // dK = s dK^T, dV = dV^T, transposed on the way out (lane = key, registers = d)
     if (my_key < N) {
-        __bf16* dkr = p.dk + head + (size_t)my_key * D;
-        __bf16* dvr = p.dv + head + (size_t)my_key * D;
+        T* dkr = (T*)p.dk + p.ldk.base(b, h, start) + (size_t)my_key * p.ldk.sn;
+        T* dvr = (T*)p.dv + p.ldv.base(b, h, start) + (size_t)my_key * p.ldv.sn;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            if (32 * db >= DH) break;          // padded columns are not stored
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                bf16x4 wk, wv;
+                V4 wk, wv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    wk[i] = (__bf16)(dka[db][4 * g + i] * p.scale);
-                    wv[i] = (__bf16)dva[db][4 * g + i];
+                    wk[i] = (T)(dka[db][4 * g + i] * p.scale);
+                    wv[i] = (T)dva[db][4 * g + i];
                 }
-                *(bf16x4*)(dkr + 32 * db + 8 * g + 4 * hi) = wk;
-                *(bf16x4*)(dvr + 32 * db + 8 * g + 4 * hi) = wv;
-            }
-    }
-}
-
-// D_i = <dO_i, O_i> in fp32, LSE_i in log2 units, and (ZERO) a zeroed dQ
-// accumulator; 8 lanes per row.
-template <int D, bool ZERO>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* o, const __bf16* dout,
-                                                      const float* lse, float* dsum, float* lse2,
-                                                      float* dq_acc, int rows) {
-    constexpr int PER = D / 8;     // elements per lane
-    const int row = blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int part = threadIdx.x & 7;
-    float acc = 0.0f;
-    if (row < rows) {
-        const size_t base = (size_t)row * D + part * PER;
-#pragma unroll
-        for (int c = 0; c < PER; c += 8) {
-            const bf16x8 a = *(const bf16x8*)(o + base + c);
-            const bf16x8 g = *(const bf16x8*)(dout + base + c);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)g[i], acc);
-            if (ZERO) {
-                *(f32x4*)(dq_acc + base + c) = f32x4{0.f, 0.f, 0.f, 0.f};
-                *(f32x4*)(dq_acc + base + c + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+                *(V4*)(dkr + 32 * db + 8 * g + 4 * hi) = wk;
+                *(V4*)(dvr + 32 * db + 8 * g + 4 * hi) = wv;
             }
         }
     }
+}
+
+// Row terms of the backward, one workspace row r = (b*H + h)*N + i per query
+// row: D_i = <dO_i, O_i> in fp32 and LSE_i in log2 units; ZERO also clears the
+// row's dQ accumulator (DZ floats). 8 lanes per row.
+struct PreParams {
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* dsum;
+    float* lse2;
+    float* dq_acc;
+    Strides lo, ldo, ll;
+    const int* cu;
+    int total, H, N, rows;
+};
+
+template <typename T, int DH, int DZ, bool ZERO>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
+    using V8 = typename Vec<T>::x8;
+    constexpr int CH = DH / 8;
+    const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    if (r >= p.rows) return;
+    if (ZERO) {
+        float* z = p.dq_acc + (size_t)r * DZ;
+#pragma unroll
+        for (int c = part * 4; c < DZ; c += 32) *(f32x4*)(z + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int bh = r / p.N, i = r - bh * p.N;
+    const int b = bh / p.H, h = bh - b * p.H;
+    int start, n;
+    sequence(p.cu, p.total, p.N, b, start, n);
+    float acc = 0.0f;
+    if (i < n) {
+        const T* orow = (const T*)p.o + p.lo.base(b, h, start) + (size_t)i * p.lo.sn;
+        const T* grow = (const T*)p.dout + p.ldo.base(b, h, start) + (size_t)i * p.ldo.sn;
+#pragma unroll
+        for (int c = part; c < CH; c += 8) {
+            const V8 a = *(const V8*)(orow + 8 * c);
+            const V8 g = *(const V8*)(grow + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)g[e], acc);
+        }
+    }
+    // The 8 lanes of a row are consecutive and every lane of the group is live
+    // (rows are whole 8-lane groups), so the exchanges stay inside the row.
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
-    if (row < rows && part == 0) {
-        dsum[row] = acc;
-        lse2[row] = lse[row] * kLog2e;
+    if (i < n && part == 0) {
+        p.dsum[r] = acc;
+        p.lse2[r] = p.lse[p.ll.base(b, h, start) + (size_t)i * p.ll.sn] * kLog2e;
     }
 }
 
-// dQ = bf16(dQ accumulator), 8 elements per thread.
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, __bf16* dq, size_t n8) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = *(const f32x4*)(acc + 8 * i);
-    const f32x4 b = *(const f32x4*)(acc + 8 * i + 4);
-    bf16x8 r;
+// dQ = element type of the fp32 accumulator (D-wide rows), DH columns stored
+// through the dQ layout; one thread per 8 elements.
+struct ConvertParams {
+    const float* acc;
+    void* dq;
+    Strides ldq;
+    const int* cu;
+    int total, H, N;
+    size_t n8;
+};
+
+template <typename T, int D, int DH>
+__global__ __launch_bounds__(256) void dq_convert_kernel(ConvertParams p) {
+    using V8 = typename Vec<T>::x8;
+    constexpr int CH = DH / 8;
+    const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= p.n8) return;
+    const size_t r = t / CH;
+    const int c = (int)(t - r * CH);
+    const int bh = (int)(r / p.N), i = (int)(r - (size_t)bh * p.N);
+    const int b = bh / p.H, h = bh - b * p.H;
+    int start, n;
+    sequence(p.cu, p.total, p.N, b, start, n);
+    if (i >= n) return;
+    const float* a = p.acc + r * D + 8 * c;
+    const f32x4 x = *(const f32x4*)a;
+    const f32x4 y = *(const f32x4*)(a + 4);
+    V8 w;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        r[t] = (__bf16)a[t];
-        r[4 + t] = (__bf16)b[t];
+    for (int e = 0; e < 4; ++e) {
+        w[e] = (T)x[e];
+        w[4 + e] = (T)y[e];
     }
-    *(bf16x8*)(dq + 8 * i) = r;
+    *(V8*)((T*)p.dq + p.ldq.base(b, h, start) + (size_t)i * p.ldq.sn + 8 * c) = w;
 }
 
-template <int D, bool CAUSAL, bool DROPOUT, bool DQ>
-hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
-    BwdParamsB p{};
-    p.q = (const __bf16*)a.q;
-    p.k = (const __bf16*)a.k;
-    p.v = (const __bf16*)a.v;
-    p.dout = (const __bf16*)a.dout;
+template <typename T, int D, int DH, bool CAUSAL, bool DROPOUT, bool DQ>
+hipError_t launch_kv_cfg(const BwdArgs& a, hipStream_t st) {
+    BwdParams p{};
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
     p.lse2 = a.lse2;
     p.dsum = a.dsum;
     p.dq_acc = a.dq_accum;
-    p.dk = (__bf16*)a.dk;
-    p.dv = (__bf16*)a.dv;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.lq = a.L.q;
+    p.lk = a.L.k;
+    p.lv = a.L.v;
+    p.ldo = a.L.dout;
+    p.ldk = a.L.dk;
+    p.ldv = a.L.dv;
+    p.cu = a.L.cu_seqlens;
+    p.total = a.L.total;
     p.H = a.s.H;
     p.N = a.s.N;
     p.nkb = (a.s.N + kBKV - 1) / kBKV;
@@ -435,51 +501,72 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
     p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 64, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, DH, 64, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
                        dim3(kNW * 64), 0, st, p);
     return hipGetLastError();
 }
 
-template <int D, bool DQ>
+template <typename T, int D, int DH, bool DQ>
 hipError_t launch_kv(const BwdArgs& a, hipStream_t st) {
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
     if (a.s.causal)
-        return drop ? launch_main<D, true, true, DQ>(a, st) : launch_main<D, true, false, DQ>(a, st);
-    return drop ? launch_main<D, false, true, DQ>(a, st) : launch_main<D, false, false, DQ>(a, st);
+        return drop ? launch_kv_cfg<T, D, DH, true, true, DQ>(a, st) : launch_kv_cfg<T, D, DH, true, false, DQ>(a, st);
+    return drop ? launch_kv_cfg<T, D, DH, false, true, DQ>(a, st) : launch_kv_cfg<T, D, DH, false, false, DQ>(a, st);
 }
 
-template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
-    const int rows = a.s.B * a.s.H * a.s.N;
-    // Without dropout the two-pass form is also the faster one (the dQ atomics
-    // cost more than recomputing S and dP once more); with dropout the Philox
-    // mask would be generated twice, and the fused form wins.
+template <typename T, int DH, int DZ, bool ZERO>
+void launch_pre(const BwdArgs& a, hipStream_t st) {
+    PreParams p{};
+    p.o = a.o;
+    p.dout = a.dout;
+    p.lse = a.lse;
+    p.dsum = a.dsum;
+    p.lse2 = a.lse2;
+    p.dq_acc = a.dq_accum;
+    p.lo = a.L.o;
+    p.ldo = a.L.dout;
+    p.ll = a.L.lse;
+    p.cu = a.L.cu_seqlens;
+    p.total = a.L.total;
+    p.H = a.s.H;
+    p.N = a.s.N;
+    p.rows = a.s.B * a.s.H * a.s.N;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, DH, DZ, ZERO>), dim3((p.rows + 31) / 32), dim3(256), 0, st, p);
+}
+
+// The two-pass backward (key side, then dQ), or with dropout the fused one with
+// dQ atomics. D: computed width; DH: stored head size.
+template <typename T, int D, int DH>
+hipError_t launch_bwd_td(const BwdArgs& a, hipStream_t st) {
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
-    if (a.deterministic || !drop) {
-        // dK, dV from the key-side pass; dQ from its own query-side pass. No
-        // atomics: every output element is written by one lane in a fixed order.
-        hipLaunchKernelGGL((bwd_pre_kernel<D, false>), dim3((rows + 31) / 32), dim3(256), 0, st,
-                           (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.dsum, a.lse2,
-                           a.dq_accum, rows);
-        const hipError_t e = launch_kv<D, false>(a, st);
+    // The fused form exists for unpadded d = 64 and 128 (its dQ atomics of d = 256
+    // would overflow the wait counter it relies on).
+    constexpr bool kFused = D == DH && D <= 128;
+    if (a.deterministic || !drop || !kFused) {
+        launch_pre<T, DH, D, false>(a, st);
+        const hipError_t e = launch_kv<T, D, DH, false>(a, st);
         if (e != hipSuccess) return e;
-        return launch_bwd_dq_bf16(a, st);
+        return launch_bwd_dq<T, D, DH>(a, st);
     }
-    hipLaunchKernelGGL((bwd_pre_kernel<D, true>), dim3((rows + 31) / 32), dim3(256), 0, st,
-                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.dsum, a.lse2,
-                       a.dq_accum, rows);
-    const hipError_t e = launch_kv<D, true>(a, st);
-    if (e != hipSuccess) return e;
-    const size_t n8 = (size_t)rows * D / 8;
-    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)a.dq_accum, (__bf16*)a.dq, n8);
-    return hipGetLastError();
+    if constexpr (kFused) {
+        launch_pre<T, DH, D, true>(a, st);
+        const hipError_t e = launch_kv<T, D, DH, true>(a, st);
+        if (e != hipSuccess) return e;
+        ConvertParams c{};
+        c.acc = a.dq_accum;
+        c.dq = a.dq;
+        c.ldq = a.L.dq;
+        c.cu = a.L.cu_seqlens;
+        c.total = a.L.total;
+        c.H = a.s.H;
+        c.N = a.s.N;
+        c.n8 = (size_t)a.s.B * a.s.H * a.s.N * (DH / 8);
+        hipLaunchKernelGGL((dq_convert_kernel<T, D, DH>), dim3((unsigned)((c.n8 + 255) / 256)), dim3(256), 0,
+                           st, c);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace
-
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
-    return a.s.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
-}
-
 }  // namespace fa

@@ -17,11 +17,56 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Element types of the matrix-core path: bf16 and fp16 share every layout
+// (16-bit elements); they differ in the product instruction, the dot product
+// of the weight sums and the float -> element rounding (both round to nearest
+// even).
+template <typename T> struct Vec;
+template <> struct Vec<__bf16> {
+    using x8 = bf16x8;
+    using x4 = bf16x4;
+    using x2 = bf16x2;
+};
+template <> struct Vec<_Float16> {
+    using x8 = f16x8;
+    using x4 = f16x4;
+    using x2 = f16x2;
+};
+
+// 32x32 output, 16-deep contraction, fp32 accumulate.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// a0 b0 + a1 b1 + c in fp32.
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
 
 #define FA_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Sequence of batch entry b: first token and length, clamped to the packed
+// rows and to N (the whole N without packed sequences).
+__device__ __forceinline__ void sequence(const int* cu, int total, int Nmax, int b, int& start, int& n) {
+    start = 0;
+    n = Nmax;
+    if (cu) {
+        start = min(max(cu[b], 0), total);
+        n = min(min(max(cu[b + 1], start), total) - start, Nmax);
+    }
+}
 
 // ---------------------------------------------------------------- buffers
 // Raw buffer resource over `bytes` bytes at `base`. Loads at or past `bytes`
@@ -50,11 +95,11 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 //   * 16 consecutive rows, same chunk (row operands, ds_read_b128);
 //   * 4 aligned rows x 64 contiguous bytes (ds_read_b64_tr_b16 of a 32-wide
 //     column block by lanes 0-31).
-// CPR = 16-byte chunks per row (8 for 128-byte rows, 16 for 256-byte rows).
+// CPR = 16-byte chunks per row (8, 16 or 32 for 128-, 256- or 512-byte rows).
 template <int CPR>
 __device__ __forceinline__ int chunk_swizzle(int row) {
-    static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
-    if (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    static_assert(CPR == 8 || CPR == 16 || CPR == 32, "rows of 128, 256 or 512 bytes");
+    if (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);   // 512-byte rows: same banks as 256
     return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
@@ -85,6 +130,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2 r;
     r[0] = (__bf16)a;   // v_cvt_pk_bf16_f32: round to nearest even
     r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typename Vec<T>::x2 r;
+    r[0] = (T)a;
+    r[1] = (T)b;
     return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {

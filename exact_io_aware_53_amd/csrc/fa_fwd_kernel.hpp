@@ -1,4 +1,4 @@
-// Forward attention for bf16 tensors on gfx950 matrix cores.
+// Forward attention for bf16 and fp16 tensors on gfx950 matrix cores.
 //
 // The method: "DL0056 FlashAttention" (intvml), "Mathematical Formulation" and
 // points (1)-(3); emergent.sh glossary "Flash Attention", "How Flash Attention
@@ -11,7 +11,7 @@
 // gfx950 mapping
 // --------------
 // * One wave owns 32 query rows. It computes the transposed score tile
-//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys of K, B = the
+//   S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (A = 32 keys of K, B = the
 //   wave's Q rows), so a lane holds 16 keys of ONE query row and its partner
 //   lane (lane ^ 32) holds the other 16: row max and row sum are in-lane
 //   reductions plus one v_permlane32_swap.
@@ -35,6 +35,14 @@
 //   Workgroups are ordered longest-first, and when B*H is a multiple of 8 the
 //   query blocks of one head are dispatched to one XCD (workgroup IDs are
 //   dealt round-robin over the 8 XCDs) so the head's K/V stays in that L2.
+// * Layouts: every tensor is addressed as a [B, H, N, d] view with its own
+//   batch, head and row strides (d contiguous), so [B, N, H, d] storage and
+//   views into packed projections need no copy. Variable-length batches pack
+//   their sequences along the token dimension (cu_seqlens offsets); a
+//   workgroup whose block lies past its sequence's end returns at once.
+// * Head sizes 32, 64, 96, 128 and 256 (the last with 64-key tiles).
+#pragma once
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
@@ -57,12 +65,15 @@ constexpr float RESCALE_SLACK = 8.0f;
 #endif
 constexpr int kPrefetch = FA_FWD_PREFETCH;
 
-struct FwdParamsB {
-    const __bf16* q;
-    const __bf16* k;
-    const __bf16* v;
-    __bf16* o;
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
     float* lse;
+    Strides lq, lk, lv, lo, ll;
+    const int* cu;    // [B + 1] token offsets of packed sequences, or null
+    int total;        // rows of the packed token dimension
     int H, N, nqb, heads;
     float sl2;        // scale * log2(e)
     float inv_keep;   // 1 / (1 - p)
@@ -95,9 +106,12 @@ __device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool r
     if (reverse) qb = nqb - 1 - qb;
 }
 
-template <int D, int BC, int NW, int RB, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1)))
-void fwd_bf16_kernel(FwdParamsB p) {
+template <typename T, int D, int BC, int NW, int RB, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && D <= 128 ? 2 : 1)))
+void fwd_kernel(FwdParams p) {
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
+    using V2 = typename Vec<T>::x2;
     constexpr int WR = 32 * RB;            // query rows per wave (RB blocks of 32)
     constexpr int BR = NW * WR;            // query rows per workgroup
     constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -124,16 +138,29 @@ void fwd_bf16_kernel(FwdParamsB p) {
     // and no long block is left to run alone at the end of the grid.
     int bh, slot;
     decode_block(blockIdx.x, p.heads, CAUSAL ? (p.nqb + 1) / 2 : p.nqb, false, bh, slot);
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    slot = __builtin_amdgcn_readfirstlane(slot);
     const int b = bh / p.H, h = bh - b * p.H;
-    const int N = p.N;
-    const size_t head = (size_t)bh * N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const auto rs_q = make_rsrc(p.q + head, head_bytes);
-    const auto rs_k = make_rsrc(p.k + head, head_bytes);
-    const auto rs_v = make_rsrc(p.v + head, head_bytes);
+    // This sequence: its first token and length (the whole N without
+    // cu_seqlens), clamped to the packed rows and to N.
+    int start, N;
+    sequence(p.cu, p.total, p.N, b, start, N);
+    const int nqb = (N + BR - 1) / BR;
+    if (slot >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;    // past this sequence's blocks
+    const T* const qh = (const T*)p.q + p.lq.base(b, h, start);
+    const T* const kh = (const T*)p.k + p.lk.base(b, h, start);
+    const T* const vh = (const T*)p.v + p.lv.base(b, h, start);
+    T* const oh = (T*)p.o + p.lo.base(b, h, start);
+    float* const lh = p.lse + p.ll.base(b, h, start);
+    // Bytes of the head's rows 0 .. N-1 (row strides >= d): every row at or past
+    // N lies beyond the range and loads as zeros.
+    const auto rs_q = make_rsrc(qh, (uint32_t)(((size_t)(N - 1) * p.lq.sn + D) * 2));
+    const auto rs_k = make_rsrc(kh, (uint32_t)(((size_t)(N - 1) * p.lk.sn + D) * 2));
+    const auto rs_v = make_rsrc(vh, (uint32_t)(((size_t)(N - 1) * p.lv.sn + D) * 2));
+    const int ldq = p.lq.sn, ldo = p.lo.sn, ldl = p.ll.sn;
 
-    const TileCopy<D, BC, PT::KCH, NW> kcopy(wave, lane);
-    const TileCopy<D, BC, PT::VCH, NW> vcopy(wave, lane);
+    const TileCopy<D, BC, PT::KCH, NW> kcopy(wave, lane, p.lk.sn);
+    const TileCopy<D, BC, PT::VCH, NW> vcopy(wave, lane, p.lv.sn);
     const int kbase = k_base<D, BC>(lane), vbase = v_base<D, BC>(lane);
 
     auto run_block = [&](int qb) {
@@ -142,13 +169,13 @@ void fwd_bf16_kernel(FwdParamsB p) {
         // Row block rb of this wave holds query rows qw + 32rb .. +31; lane's row: qw + 32rb + l32.
 
         // ---- Q rows as B operands: chunk c holds d = 16c + 8*hi .. +7
-        bf16x8 qreg[RB][D / 16];
+        V8 qreg[RB][D / 16];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int c = 0; c < D / 16; ++c)
                 qreg[rb][c] = __builtin_bit_cast(
-                    bf16x8, buffer_load16(rs_q, (uint32_t)((qw + 32 * rb + l32) * D + 16 * c + 8 * hi) * 2));
+                    V8, buffer_load16(rs_q, (uint32_t)((qw + 32 * rb + l32) * ldq + 16 * c + 8 * hi) * 2));
 
         f32x16 oacc[RB][DB];
 #pragma unroll
@@ -201,23 +228,22 @@ void fwd_bf16_kernel(FwdParamsB p) {
             // them the compiler sinks each read to just before its product.
             f32x16 s[RB][KB];
             {
-                bf16x8 kop[kPrefetch];
+                V8 kop[kPrefetch];
 #pragma unroll
-                for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC>(kt, kbase, j);
+                for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC, V8>(kt, kbase, j);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < S_MFMA; ++i) {
                     const int kb = i % KB, c = i / KB;
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % kPrefetch], qreg[rb][c],
-                                                                            c == 0 ? f32x16{} : s[rb][kb], 0, 0, 0);
-                    if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC>(kt, kbase, i + kPrefetch);
+                        s[rb][kb] = mfma32(kop[i % kPrefetch], qreg[rb][c], c == 0 ? f32x16{} : s[rb][kb]);
+                    if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC, V8>(kt, kbase, i + kPrefetch);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
 
-            bf16x8 pb[RB][NC];
+            V8 pb[RB][NC];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int row0 = qw + 32 * rb;     // first row of the block
@@ -266,7 +292,7 @@ void fwd_bf16_kernel(FwdParamsB p) {
                     }
                 }
                 const float neg = -m2[rb];
-                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+                const V2 ones = {(T)1.0f, (T)1.0f};
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -275,13 +301,13 @@ void fwd_bf16_kernel(FwdParamsB p) {
                         const float x1 = fast_exp2(fmaf(s[rb][kb][r + 1], p.sl2, neg));
                         lsum[rb] += x0;
                         lsum[rb] += x1;
-                        bf16x2 w;
-                        w[0] = (__bf16)x0;
-                        w[1] = (__bf16)x1;
-                        lbf[rb] = __builtin_amdgcn_fdot2_f32_bf16(w, ones, lbf[rb], false);
+                        V2 w;
+                        w[0] = (T)x0;
+                        w[1] = (T)x1;
+                        lbf[rb] = dot2(w, ones, lbf[rb]);
                         if (DROPOUT) {
-                            w[0] = (__bf16)((keep[kb] >> r) & 1u ? x0 : 0.0f);
-                            w[1] = (__bf16)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
+                            w[0] = (T)((keep[kb] >> r) & 1u ? x0 : 0.0f);
+                            w[1] = (T)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
                         }
                         const int pc = kb * 2 + r / 8, pi = r % 8;
                         pb[rb][pc][pi] = w[0];
@@ -291,17 +317,16 @@ void fwd_bf16_kernel(FwdParamsB p) {
 
             // ---- O~^T += V^T P^T; each V^T operand read feeds the RB row blocks
             {
-                bf16x8 vop[kPrefetch];
+                V8 vop[kPrefetch];
 #pragma unroll
-                for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC>(vt, vbase, j);
+                for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC, V8>(vt, vbase, j);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < PV_MFMA; ++j) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        oacc[rb][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j % kPrefetch], pb[rb][j / DB],
-                                                                                   oacc[rb][j % DB], 0, 0, 0);
-                    if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC>(vt, vbase, j + kPrefetch);
+                        oacc[rb][j % DB] = mfma32(vop[j % kPrefetch], pb[rb][j / DB], oacc[rb][j % DB]);
+                    if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC, V8>(vt, vbase, j + kPrefetch);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -315,23 +340,23 @@ void fwd_bf16_kernel(FwdParamsB p) {
             const float lbtot = add_with_partner32(lbf[rb]);
             const float inv = p.inv_keep / lbtot;
             if (my_q < N) {
-                __bf16* orow = p.o + head + (size_t)my_q * D;
+                T* orow = oh + (size_t)my_q * ldo;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        bf16x4 w;
+                        V4 w;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(oacc[rb][db][4 * g + i] * inv);
-                        *(bf16x4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
+                        for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[rb][db][4 * g + i] * inv);
+                        *(V4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
                     }
-                if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m2[rb] + fast_log2(ltot)) * kLn2;
+                if (hi == 0) lh[(size_t)my_q * ldl] = (m2[rb] + fast_log2(ltot)) * kLn2;
             }
         }
     };
 
     if (CAUSAL) {
-        const int longer = p.nqb - 1 - slot;
+        const int longer = nqb - 1 - slot;
         run_block(longer);
         if (slot != longer) {
             __syncthreads();     // every wave is done with the buffers the next block refills
@@ -344,6 +369,9 @@ void fwd_bf16_kernel(FwdParamsB p) {
 
 // Keys per K/V tile and waves (32 query rows each) per workgroup: 128-key tiles
 // and 8 waves, one workgroup per CU (two waves per SIMD) sharing each K/V copy.
+// d = 256 takes 64-key tiles (two 128-key K/V tiles would not fit in LDS) and
+// 4 waves with up to 512 registers each: the Q rows (64 registers) and the
+// output accumulator (128) leave too little of 256 for the score tile.
 #ifndef FA_FWD_BC
 #define FA_FWD_BC 128
 #endif
@@ -355,15 +383,23 @@ void fwd_bf16_kernel(FwdParamsB p) {
 #define FA_FWD_RB 1
 #endif
 
-template <int D, bool CAUSAL, bool DROPOUT>
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-    constexpr int BC = FA_FWD_BC, NW = FA_FWD_NW, RB = FA_FWD_RB, BR = NW * 32 * RB;
-    FwdParamsB p{};
-    p.q = (const __bf16*)a.q;
-    p.k = (const __bf16*)a.k;
-    p.v = (const __bf16*)a.v;
-    p.o = (__bf16*)a.o;
+    constexpr int BC = D == 256 ? 64 : FA_FWD_BC, NW = D == 256 ? 4 : FA_FWD_NW, RB = FA_FWD_RB;
+    constexpr int BR = NW * 32 * RB;
+    FwdParams p{};
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.o;
     p.lse = a.lse;
+    p.lq = a.L.q;
+    p.lk = a.L.k;
+    p.lv = a.L.v;
+    p.lo = a.L.o;
+    p.ll = a.L.lse;
+    p.cu = a.L.cu_seqlens;
+    p.total = a.L.total;
     p.H = a.s.H;
     p.N = a.s.N;
     p.nqb = (a.s.N + BR - 1) / BR;
@@ -373,22 +409,18 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
     const int blocks = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * blocks),
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * blocks),
                        dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
-    if (a.s.causal) return drop ? launch_cfg<D, true, true>(a, st) : launch_cfg<D, true, false>(a, st);
-    return drop ? launch_cfg<D, false, true>(a, st) : launch_cfg<D, false, false>(a, st);
+    if (a.s.causal) return drop ? launch_cfg<T, D, true, true>(a, st) : launch_cfg<T, D, true, false>(a, st);
+    return drop ? launch_cfg<T, D, false, true>(a, st) : launch_cfg<T, D, false, false>(a, st);
 }
+
 
 }  // namespace
-
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-    return a.s.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
-}
-
 }  // namespace fa

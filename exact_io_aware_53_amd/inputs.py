@@ -176,3 +176,70 @@ def sample_rows(w: Workload, count: int, block_rows=(128,)):
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact fp64 copy of a CPU tensor (bf16 and fp32 widen exactly)."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+# Coverage workloads: head sizes, fp16, [B, N, H, d] storage and packed
+# variable-length batches, each at a size that fills the GPU.
+@dataclass(frozen=True)
+class CoverageWorkload:
+    name: str
+    B: int                # batch entries (sequences for "varlen")
+    H: int
+    N: int                # sequence length; for "varlen" the longest allowed
+    d: int
+    dtype: str            # "bf16" or "fp16"
+    layout: str           # "bhsd", "bshd" or "varlen"
+    causal: bool = True
+    data_seed: int = 0
+    len_lo: int = 0       # "varlen": lengths uniform in [len_lo, N]
+    head_seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.d))
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float16
+
+    def lengths(self) -> np.ndarray:
+        if self.layout != "varlen":
+            return np.full(self.B, self.N, dtype=np.int64)
+        rng = np.random.Generator(np.random.PCG64(self.data_seed + 1))
+        return rng.integers(self.len_lo, self.N + 1, size=self.B)
+
+    def fwd_flops(self) -> float:
+        """4 * H * n^2 * d per sequence, halved when causal."""
+        f = float(sum(4.0 * self.H * int(n) * int(n) * self.d for n in self.lengths()))
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        return 2.5 * self.fwd_flops()
+
+
+COVERAGE_WORKLOADS = {
+    w.name: w for w in [
+        CoverageWorkload("cov_d256_bf16_b2h16n4096", 2, 16, 4096, 256, "bf16", "bhsd", data_seed=1101),
+        CoverageWorkload("cov_d96_bf16_b2h16n4096", 2, 16, 4096, 96, "bf16", "bhsd", data_seed=1102),
+        CoverageWorkload("cov_d32_bf16_b2h16n4096", 2, 16, 4096, 32, "bf16", "bhsd", data_seed=1103),
+        CoverageWorkload("cov_fp16_b2h32n8192d128", 2, 32, 8192, 128, "fp16", "bhsd", data_seed=1104),
+        CoverageWorkload("cov_bshd_bf16_b2h32n8192d128", 2, 32, 8192, 128, "bf16", "bshd", data_seed=1105),
+        CoverageWorkload("cov_varlen_bf16_32seq_h16d128", 32, 16, 4096, 128, "bf16", "varlen",
+                         data_seed=1106, len_lo=128),
+    ]
+}
+
+
+def make_coverage_inputs(w: CoverageWorkload):
+    """Q, K, V, dO as CPU tensors in the workload's storage: [B, H, N, d] ("bhsd"),
+    [B, N, H, d] ("bshd"), or packed [total, H, d] with cu_seqlens [B+1] int32
+    ("varlen"). Values drawn as in normal_tensors, in the storage shape."""
+    if w.layout == "varlen":
+        lens = w.lengths()
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ts = normal_tensors((int(cu[-1]), w.H, w.d), w.data_seed, 4, w.torch_dtype)
+        out = dict(zip(("q", "k", "v", "do"), ts))
+        out["cu_seqlens"] = torch.from_numpy(cu)
+        return out
+    shape = (w.B, w.N, w.H, w.d) if w.layout == "bshd" else (w.B, w.H, w.N, w.d)
+    return dict(zip(("q", "k", "v", "do"), normal_tensors(shape, w.data_seed, 4, w.torch_dtype)))

@@ -34,7 +34,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, d] arrays, d
- *   fastest (row-major), element type given by the symbol (bf16 or fp32).
+ *   fastest (row-major), element type given by the symbol (bf16 or fp32);
+ *   fa_fwd_ex and fa_bwd_ex take strided views, fp16 and packed batches.
  *   LSE is a contiguous [B, H, N] fp32 array. Every tensor pointer must be
  *   16-byte aligned.
  * - Memory: every pointer is device memory owned by the caller. The library
@@ -47,8 +48,10 @@
  *   FA_ERR_INVALID_ARG  null pointer, B/H/N < 1, dropout_p outside [0, 1),
  *                       scale not a positive finite number, misaligned
  *                       pointer, too small a workspace, B*H*N*d above
- *                       2^31 - 1.
- *   FA_ERR_UNSUPPORTED  head size d other than 64 or 128 (the caller keeps its
+ *                       2^31 - 1, or one head's rows past 32-bit offsets
+ *                       ((N + 256) * d * 4 >= 0xf0000000).
+ *   FA_ERR_UNSUPPORTED  head size d other than 64 or 128 (fa_fwd_ex and fa_bwd_ex
+ *                       also take 32, 96 and 256; the caller keeps its
  *                       own fallback, as emergent.sh "How to Enable Flash
  *                       Attention Safely", step 7, advises).
  *   FA_ERR_HIP          a HIP launch error; the stream state is unspecified.
@@ -137,6 +140,80 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  * Returns 0 if an argument is out of range.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * General layouts, element types, head sizes and variable-length batches.
+ * The pages list tensor layouts, head sizes, numeric precision, padding and
+ * uneven sequence lengths among what decides whether an attention kernel
+ * applies (emergent.sh glossary "Flash Attention", "Practical Limits and
+ * Common Pitfalls" and "How to Enable Flash Attention Safely", step 3). The
+ * _ex entry points compute the same operation as fa_fwd / fa_bwd on:
+ *   - bf16 or fp16 tensors (fp32 accumulation and softmax either way);
+ *   - head size d in {32, 64, 96, 128, 256};
+ *   - any strided [B, H, N, d] view with d contiguous: each tensor has its own
+ *     batch, head and row strides in elements, for example [B, N, H, d]
+ *     storage (row stride H*d, head stride d) or views into a packed QKV
+ *     projection (row stride 3*H*d);
+ *   - packed variable-length batches: with cu_seqlens non-NULL, sequence b is
+ *     rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the token dimension of every
+ *     tensor (row stride as given, batch stride ignored); its element (h, i)
+ *     lives at base + h * head + (cu_seqlens[b] + i) * row. Causal masking,
+ *     the dropout counter (b, h, i, j) and LSE are per sequence, i and j
+ *     counted from the sequence's first token.
+ */
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 } fa_dtype;
+
+/* Element strides of one tensor seen as [B, H, N, d] (d contiguous). */
+typedef struct {
+    int64_t batch;
+    int64_t head;
+    int64_t row;
+} fa_layout;
+
+typedef struct {
+    int B, H;
+    int N;                  /* sequence length; with cu_seqlens, an upper bound on every length */
+    int d;                  /* 32, 64, 96, 128 or 256 */
+    int dtype;              /* fa_dtype of q, k, v, o, dout, dq, dk, dv */
+    const int32_t* cu_seqlens;  /* device int32 [B + 1], or NULL */
+    int total_tokens;       /* with cu_seqlens: rows of the packed token dimension */
+    fa_layout q, k, v, o;   /* 16-bit tensors */
+    fa_layout lse;          /* fp32 LSE as a [B, H, N] view (d = 1) */
+    fa_layout dout, dq, dk, dv;   /* backward only */
+} fa_problem;
+
+/*
+ * Checks on the host (FA_ERR_INVALID_ARG otherwise): B, H, N >= 1; row
+ * strides >= d and, like head and batch strides, non-negative multiples of 8
+ * elements for the 16-bit tensors (16-byte aligned rows); LSE strides
+ * non-negative, its row stride >= 1; every head's rows 0 .. N+255 within
+ * 0xf0000000 bytes ((N + 256) * row * element size); total_tokens >= 1
+ * with cu_seqlens. FA_ERR_UNSUPPORTED: d or dtype outside the lists above.
+ * cu_seqlens is read on the device: each sequence is clamped to
+ * [0, total_tokens) rows and to at most N rows, so out-of-order or oversized
+ * entries cannot make a kernel touch memory outside the tensors; its contents
+ * are otherwise the caller's contract (non-decreasing, cu_seqlens[0] = 0).
+ * Outputs of padded rows (those no sequence covers) are not written.
+ */
+int fa_fwd_ex(const fa_problem* problem, const void* q, const void* k, const void* v, void* o,
+              float* lse, float scale, int causal, float dropout_p, uint64_t seed, void* stream);
+
+/*
+ * Backward of fa_fwd_ex on the same problem (O and LSE as fa_fwd_ex wrote
+ * them). deterministic != 0 asks for the two-pass form of fa_bwd_deterministic
+ * (always taken without dropout, and for d in {32, 96, 256}); otherwise dQ is
+ * summed with fp32 atomics when dropout is on. Head sizes 32 and 96 compute
+ * on rows padded with zeros to 64 and 128 (exact; the products take the
+ * padded width). workspace: fa_bwd_ex_workspace_size(problem) bytes, 256-byte
+ * aligned.
+ */
+int fa_bwd_ex(const fa_problem* problem, const void* q, const void* k, const void* v,
+              const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+              float scale, int causal, float dropout_p, uint64_t seed, int deterministic,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch fa_bwd_ex needs for this problem (0 if invalid). */
+size_t fa_bwd_ex_workspace_size(const fa_problem* problem);
 
 /*
  * Decode-shaped forward, bf16: Nq query rows against Nk key/value rows of the
