@@ -31,6 +31,13 @@
 namespace fa {
 namespace {
 
+#ifndef FA_DQ_PF
+#define FA_DQ_PF 2
+#endif
+#ifndef FA_DQ_TF
+#define FA_DQ_TF 4
+#endif
+
 struct DqParams {
     const void* q;
     const void* k;
@@ -91,6 +98,9 @@ void bwd_dq_kernel(DqParams p) {
     constexpr int CH = D / 8, ROW = D * 2;
     constexpr int KB = BC / 32, NC = BC / 16, DB = D / 32, NCD = D / 16;
     constexpr int TILE = BC * D * 2;
+    // LDS operand reads in flight ahead of their products (score and dP
+    // products: pairs of K and V reads; dQ products: K^T reads).
+    constexpr int kPf = FA_DQ_PF, kTf = FA_DQ_TF;
 
     __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
     __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE];
@@ -192,15 +202,31 @@ void bwd_dq_kernel(DqParams p) {
             const int k0 = t * BC;
 
             // S^T = K Q^T and dP^T = V dO^T; element (kb, r): key 32kb + 8(r/4) + 4hi + r%4, row my_q
+            // Operand reads run kPf steps ahead of their products; the scheduling
+            // fences keep them there (the compiler would sink each read to its use).
             f32x16 s[KB], dp[KB];
+            {
+                constexpr int SI = NCD * KB;
+                auto ldo = [&](int i) { return roff[i / KB] + (i % KB) * 32 * ROW; };
+                V8 ka[kPf], va[kPf];
 #pragma unroll
-            for (int c = 0; c < NCD; ++c)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int o = roff[c] + kb * 32 * ROW;
-                    s[kb] = mfma32(*(const FA_LDS V8*)(kt + o), qreg[c], c == 0 ? f32x16{} : s[kb]);
-                    dp[kb] = mfma32(*(const FA_LDS V8*)(vt + o), doreg[c], c == 0 ? f32x16{} : dp[kb]);
+                for (int j = 0; j < kPf; ++j) {
+                    ka[j] = *(const FA_LDS V8*)(kt + ldo(j));
+                    va[j] = *(const FA_LDS V8*)(vt + ldo(j));
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < SI; ++i) {
+                    const int c = i / KB, kb = i % KB;
+                    s[kb] = mfma32(ka[i % kPf], qreg[c], c == 0 ? f32x16{} : s[kb]);
+                    dp[kb] = mfma32(va[i % kPf], doreg[c], c == 0 ? f32x16{} : dp[kb]);
+                    if (i + kPf < SI) {
+                        ka[i % kPf] = *(const FA_LDS V8*)(kt + ldo(i + kPf));
+                        va[i % kPf] = *(const FA_LDS V8*)(vt + ldo(i + kPf));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             // log2 P = s * scale * log2(e) - LSE_i * log2(e); masked elements -> -inf
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -235,18 +261,28 @@ void bwd_dq_kernel(DqParams p) {
                     dsb[pc][pi + 1] = (T)ds[1];
                 }
             // dQ^T += K^T dS^T over the tile's 16-key chunks
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
+            {
+                constexpr int QI = NC * DB;
+                auto ldt = [&](int j) {    // K^T operand of step j = c * DB + db
+                    const int c = j / DB, db = j % DB;
                     const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (FA_LDS s16x4*)(kt + troff[db][0] + 16 * c * ROW));
                     const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (FA_LDS s16x4*)(kt + troff[db][1] + 16 * c * ROW));
                     typedef short s16x8 __attribute__((ext_vector_type(8)));
-                    const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    dqa[db] = mfma32(a, dsb[c], dqa[db]);
+                    return __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+                };
+                V8 ta[kTf];
+#pragma unroll
+                for (int j = 0; j < kTf; ++j) ta[j] = ldt(j);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < QI; ++j) {
+                    dqa[j % DB] = mfma32(ta[j % kTf], dsb[j / DB], dqa[j % DB]);
+                    if (j + kTf < QI) ta[j % kTf] = ldt(j + kTf);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            }
         }
 
         if (my_q < N) {

@@ -47,6 +47,13 @@
 namespace fa {
 namespace {
 
+#ifndef FA_KV_PF
+#define FA_KV_PF 2
+#endif
+#ifndef FA_KV_TF
+#define FA_KV_TF 2
+#endif
+
 constexpr int kBKV = 128;     // keys per workgroup
 constexpr int kNW = 4;        // waves per workgroup (32 keys each)
 
@@ -108,6 +115,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     static_assert(!DQ || DQ_ATOMICS <= 63, "vmcnt holds at most 63");
 
     constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
+    // LDS operand pairs in flight ahead of their products (S/dP, then dV/dK).
+    constexpr int kPf = FA_KV_PF, kTf = FA_KV_TF;
     __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char k_s[DQ ? kBKV * D * 2 : 16];
@@ -259,16 +268,41 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                     *(FA_LDS u32x2*)(dsL + tile_offset<BQ / 8>(wave * 32 + l32, qb * 32 + 8 * g + 4 * hi)) =
                         u32x2{0u, 0u};
         } else {
+            // LDS operand reads run kPf steps ahead of their products; the
+            // scheduling fences keep them there (one wave per SIMD here, so
+            // nothing else hides their latency).
             f32x16 s[QB], dp[QB];
+            if constexpr (DQ) {
+                // the fused form: the compiler's own order measured faster here
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
+                for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.0f;
+                    for (int c = 0; c < NCD; ++c) {
+                        const int o = roff[c] + qb * 32 * ROW;
+                        s[qb] = mfma32(*(const FA_LDS V8*)(qT + o), kt[c], c == 0 ? f32x16{} : s[qb]);
+                        dp[qb] = mfma32(*(const FA_LDS V8*)(doT + o), vt[c], c == 0 ? f32x16{} : dp[qb]);
+                    }
+                }
+            } else {
+                constexpr int SI = QB * NCD;
+                auto so = [&](int i) { return roff[i % NCD] + (i / NCD) * 32 * ROW; };
+                V8 qa[kPf], da[kPf];
 #pragma unroll
-                for (int c = 0; c < NCD; ++c) {
-                    const int o = roff[c] + qb * 32 * ROW;
-                    s[qb] = mfma32(*(const FA_LDS V8*)(qT + o), kt[c], s[qb]);
-                    dp[qb] = mfma32(*(const FA_LDS V8*)(doT + o), vt[c], dp[qb]);
+                for (int j = 0; j < kPf; ++j) {
+                    qa[j] = *(const FA_LDS V8*)(qT + so(j));
+                    da[j] = *(const FA_LDS V8*)(doT + so(j));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < SI; ++i) {
+                    const int qb = i / NCD, c = i % NCD;
+                    s[qb] = mfma32(qa[i % kPf], kt[c], c == 0 ? f32x16{} : s[qb]);
+                    dp[qb] = mfma32(da[i % kPf], vt[c], c == 0 ? f32x16{} : dp[qb]);
+                    if (i + kPf < SI) {
+                        qa[i % kPf] = *(const FA_LDS V8*)(qT + so(i + kPf));
+                        da[i % kPf] = *(const FA_LDS V8*)(doT + so(i + kPf));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
@@ -309,19 +343,50 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                     dp[qb][r] = ds;         // dS
                 }
             // dV^T += dO^T (P Z'),  dK^T += Q^T dS  (contraction over the tile's query rows)
+            if constexpr (DQ) {
 #pragma unroll
-            for (int qc = 0; qc < BQ / 16; ++qc) {
+                for (int qc = 0; qc < BQ / 16; ++qc) {
+                    V8 bp, bs;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
+                        bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
+                    }
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
+                        dva[db] = mfma32(tr_read<V8>(doT, o0, o1), bp, dva[db]);
+                        dka[db] = mfma32(tr_read<V8>(qT, o0, o1), bs, dka[db]);
+                    }
+                }
+            } else {
+                constexpr int TI = (BQ / 16) * DB;     // steps j = qc * DB + db
+                auto to = [&](int j, int half) { return troff[j % DB][half] + 16 * (j / DB) * ROW; };
+                V8 oa[kTf], ta[kTf];
+#pragma unroll
+                for (int j = 0; j < kTf; ++j) {
+                    oa[j] = tr_read<V8>(doT, to(j, 0), to(j, 1));
+                    ta[j] = tr_read<V8>(qT, to(j, 0), to(j, 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 V8 bp, bs;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
-                    bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
-                }
+                for (int j = 0; j < TI; ++j) {
+                    const int qc = j / DB, db = j % DB;
+                    if (db == 0) {
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
-                    dva[db] = mfma32(tr_read<V8>(doT, o0, o1), bp, dva[db]);
-                    dka[db] = mfma32(tr_read<V8>(qT, o0, o1), bs, dka[db]);
+                        for (int i = 0; i < 8; ++i) {
+                            bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
+                            bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
+                        }
+                    }
+                    dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
+                    dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
+                    if (j + kTf < TI) {
+                        oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
+                        ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
