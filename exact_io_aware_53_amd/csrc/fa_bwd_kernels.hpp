@@ -109,20 +109,22 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     constexpr int QLOADS = BQ * CH / (64 * kNW);
     constexpr int KLOADS = kBKV * CH / (64 * kNW);
     static_assert(QLOADS * 64 * kNW == BQ * CH, "query tile must split over the waves");
-    static_assert(BQ == 64, "dS^T rows need 8 chunks for the swizzle");
+    static_assert(!DQ || BQ == 64, "dS^T rows need 8 chunks for the swizzle");
+    static_assert(BQ == 32 || BQ == 64, "query tiles of 32 or 64 rows");
     static_assert((QB * DB) % kNW == 0, "dQ blocks must split evenly over the waves");
     constexpr int DQ_ATOMICS = (QB * DB / kNW) * 16;   // dQ atomics per lane per tile
     static_assert(!DQ || DQ_ATOMICS <= 63, "vmcnt holds at most 63");
 
     constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
     // LDS operand pairs in flight ahead of their products (S/dP, then dV/dK).
-    constexpr int kPf = FA_KV_PF, kTf = FA_KV_TF;
+    constexpr int kPf = D == 256 ? 1 : FA_KV_PF, kTf = D == 256 ? 1 : FA_KV_TF;
     __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char k_s[DQ ? kBKV * D * 2 : 16];
     __shared__ __attribute__((aligned(1024))) char dst_s[DQ ? kBKV * BQ * 2 : 16];
-    __shared__ float lse_s[NBUF * BQ];
-    __shared__ float dsum_s[NBUF * BQ];
+    // Row terms: 64 per buffer slot whatever BQ (one per lane of the copying wave).
+    __shared__ float lse_s[NBUF * 64];
+    __shared__ float dsum_s[NBUF * 64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -186,8 +188,10 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) troff[db][half] = tile_offset<CH>(tr_row + 8 * half, 32 * db + tr_col);
+        if constexpr (DQ) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) tsoff[qb][half] = tile_offset<BQ / 8>(tr_row + 8 * half, 32 * qb + tr_col);
+            for (int qb = 0; qb < QB; ++qb) tsoff[qb][half] = tile_offset<BQ / 8>(tr_row + 8 * half, 32 * qb + tr_col);
+        }
     }
     constexpr int ROW = D * 2, SROW = BQ * 2;     // LDS row bytes: Q/dO/K tiles, dS^T tile
 
@@ -225,10 +229,10 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
             buffer_to_lds16(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldo));
         }
         if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)(lse_s + buf * BQ), 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)(lse_s + buf * 64), 4,
                                                      (uint32_t)(i0 + lane) * 4, 0, 0, 0);
         if (wave == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)(dsum_s + buf * BQ), 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)(dsum_s + buf * 64), 4,
                                                      (uint32_t)(i0 + lane) * 4, 0, 0, 0);
     };
 
@@ -254,13 +258,16 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
         if (!DQ && i0 > i_first) issue_tile(i0 - BQ, buf ^ 1);   // the other buffer: read last tile
         const FA_LDS char* const qT = qL + buf * TILE;
         const FA_LDS char* const doT = doL + buf * TILE;
-        const float* const lse_t = lse_s + buf * BQ;
-        const float* const dsum_t = dsum_s + buf * BQ;
+        const float* const lse_t = lse_s + buf * 64;
+        const float* const dsum_t = dsum_s + buf * 64;
 
-        const bool skip = CAUSAL && kw > i0 + BQ - 1;    // every query of the tile precedes our keys
+        // Every query of the tile precedes our keys. (d = 256 runs such tiles fully
+        // masked instead: their zero contributions cost less than the register
+        // shuffling a second path through the loop costs at 512 registers.)
+        const bool skip = CAUSAL && D != 256 && kw > i0 + BQ - 1;
         if (skip) {
             // this wave's rows of dS^T are zero for this tile
-            if (DQ)
+            if constexpr (DQ)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
-            if (DQ)
+            if constexpr (DQ)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -566,7 +573,10 @@ hipError_t launch_kv_cfg(const BwdArgs& a, hipStream_t st) {
     p.inv_keep = 1.0f / (1.0f - a.s.dropout_p);
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, DH, 64, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
+    // d = 256: 32-row query tiles, so that K, V, dK, dV of a wave's 32 keys and
+    // the score tile fit in the 512 registers of a lane.
+    constexpr int BQ = D == 256 ? 32 : 64;
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, DH, BQ, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
                        dim3(kNW * 64), 0, st, p);
     return hipGetLastError();
 }
