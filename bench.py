@@ -8,7 +8,8 @@ forward (B=2, H=32, N=8192, d=128, Q scaled by 4). The same JSON line also
 carries the forward+backward measurement on the dropout workload
 (B=2, H=16, N=4096, d=64, p=0.1; the backward in both its fused atomic form
 and its two-pass deterministic form), the backward at the default workload's
-shape, the decode-shaped forward on its three workloads (HBM-bound: GB/s
+shape, the long-context forward (B=1, H=16, N=32768, d=128) with an N sweep
+and the device memory each call takes, the decode-shaped forward on its three workloads (HBM-bound: GB/s
 against 8 TB/s), the general entry points on head sizes 32/96/256, fp16,
 [B, N, H, d] storage and a packed variable-length batch (`coverage`), the
 roofline of the dominant kernel and the CPU oracle's throughput on a bounded
@@ -35,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "fwd_causal_q4_bf16_b2h32n8192d128"
 FWD_BWD_WORKLOAD = "fwdbwd_causal_dropout_bf16_b2h16n4096d64"
+LONG_WORKLOAD = "fwd_causal_bf16_b1h16n32768d128"
 FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd.hip", "exact_io_aware_53_amd/csrc/fa_fwd_kernel.hpp",
                "exact_io_aware_53_amd/csrc/fa_device.hpp", "exact_io_aware_53_amd/csrc/fa_tiles.hpp",
                "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
@@ -122,6 +124,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-bwd", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context forward and its N sweep")
     ap.add_argument("--no-coverage", action="store_true",
                     help="skip the head-size / fp16 / layout / packed-batch measurements")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -243,6 +246,42 @@ def main():
                        "tflops_bwd": round(w.bwd_flops() / (t3 * 1e-3) / 1e12, 3),
                        "frac": round(w.bwd_flops() / (t3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del do3, dq3, dk3, dv3, ws3
+
+    if not args.no_long:
+        # Long-context forward (B1 H16 N32768 d128 causal) and an N sweep at the same
+        # B, H, d: time, and device memory the call itself takes (free memory read
+        # by hipMemGetInfo around it, outputs preallocated): zero at every N.
+        wl = WORKLOADS[LONG_WORKLOAD]
+        sweep = []
+        for n in (4096, 8192, 16384, wl.N):
+            hl = make_inputs(wl, with_grad_out=False) if n == wl.N else None
+            if hl is None:
+                from exact_io_aware_53_amd.inputs import normal_tensors
+                ql, kl, vl = (x.to(dev) for x in normal_tensors((wl.B, wl.H, n, wl.d), wl.data_seed, 3,
+                                                                  torch.bfloat16))
+            else:
+                ql, kl, vl = (hl[x].to(dev) for x in ("q", "k", "v"))
+                del hl
+            ol = torch.empty_like(ql)
+            ll = torch.empty((wl.B, wl.H, n), dtype=torch.float32, device=dev)
+
+            def fl():
+                fa.fwd(ql, kl, vl, scale=wl.scale, causal=True, out=ol, lse=ll)
+
+            fl()
+            torch.cuda.synchronize()
+            free0 = torch.cuda.mem_get_info(dev)[0]
+            _, evl = time_launches(fl, max(5, args.steps // 3), 2, stream)
+            free1 = torch.cuda.mem_get_info(dev)[0]
+            ml = sum(evl) / len(evl)
+            fl_flops = 4.0 * wl.B * wl.H * n * n * wl.d / 2
+            sweep.append({"N": n, "ms": round(ml, 4), "tflops": round(fl_flops / (ml * 1e-3) / 1e12, 3),
+                          "tensor_bytes": 4 * wl.B * wl.H * n * wl.d * 2 + 4 * wl.B * wl.H * n,
+                          "call_device_bytes": int(free0 - free1)})
+            del ql, kl, vl, ol, ll
+            torch.cuda.empty_cache()
+        line["long_context"] = {"workload": wl.name, "sweep": sweep,
+                                "s_matrix_bytes_avoided_bf16": 2 * wl.B * wl.H * wl.N * wl.N}
 
     if not args.no_decode:
         from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs

@@ -295,3 +295,25 @@ def test_uniform_scores_and_causal_row0_on_gpu():
     q2 = normal_tensors((B, H, N, d), 9120, 1, torch.bfloat16)[0]
     o2, _ = fa.fwd(*upload((q2, k, v)), causal=True)
     assert torch.equal(o2[0, 0, 0].cpu(), v[0, 0, 0])
+
+
+def test_forward_takes_no_device_memory_and_inputs_grow_linearly():
+    """The forward needs no workspace: with outputs preallocated, free device
+    memory is the same before and after a call at every N; the tensors a call
+    touches grow linearly in N (no N x N buffer exists anywhere)."""
+    B, H, d = 1, 4, 128
+    sizes = []
+    for N in (1024, 4096, 16384):
+        q, k, v = (t.cuda() for t in normal_tensors((B, H, N, d), 9300 + N, 3, torch.bfloat16))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        for _ in range(3):
+            fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.cuda.mem_get_info()[0] == free0
+        sizes.append(sum(t.numel() * t.element_size() for t in (q, k, v, o, lse)))
+        del q, k, v, o, lse
+    assert sizes[1] == 4 * sizes[0] and sizes[2] == 4 * sizes[1]
