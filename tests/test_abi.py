@@ -153,3 +153,76 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         fa.lib()
+
+
+def problem(**kw):
+    """A valid contiguous bf16 problem, then the overrides."""
+    B, H, N, d = kw.pop("B", 2), kw.pop("H", 3), kw.pop("N", 100), kw.pop("d", 64)
+    lay = fa.Layout(H * N * d, N * d, d)
+    pb = fa.Problem(B=B, H=H, N=N, d=d, dtype=kw.pop("dtype", 0), cu_seqlens=kw.pop("cu", None),
+                    total_tokens=kw.pop("total", 0))
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        setattr(pb, name, lay)
+    pb.lse = fa.Layout(H * N, N, 1)
+    for name, val in kw.items():
+        setattr(pb, name, val)
+    return pb
+
+
+def fwd_ex(L, pb, scale=0.125, p=0.0, lse=FAKE):
+    return L.fa_fwd_ex(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, lse, scale, 1, p, 0, None)
+
+
+def bwd_ex(L, pb, ws_bytes=None, ws=FAKE * 16):
+    need = L.fa_bwd_ex_workspace_size(ctypes.byref(pb))
+    return L.fa_bwd_ex(ctypes.byref(pb), *([FAKE] * 9), 0.125, 1, 0.0, 0, 1, ws,
+                       need if ws_bytes is None else ws_bytes, None)
+
+
+def test_ex_rejects_invalid_problems(L):
+    inv, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    assert L.fa_fwd_ex(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 0, 0.0, 0, None) == inv
+    for d in (16, 48, 80, 160, 512):
+        assert fwd_ex(L, problem(d=d)) == uns
+    assert fwd_ex(L, problem(dtype=2)) == uns
+    for bad in (dict(B=0), dict(H=-1), dict(N=0)):
+        assert fwd_ex(L, problem(**bad)) == inv
+    N, d = 100, 64
+    assert fwd_ex(L, problem(q=fa.Layout(0, N * d, d - 8))) == inv            # rows overlap
+    assert fwd_ex(L, problem(k=fa.Layout(0, N * d + 4, d))) == inv            # head stride not 16-byte
+    assert fwd_ex(L, problem(v=fa.Layout(-8, N * d, d))) == inv               # negative stride
+    assert fwd_ex(L, problem(o=fa.Layout(0, N * d, d + 4))) == inv            # row stride not 16-byte
+    assert fwd_ex(L, problem(lse=fa.Layout(0, N, 0))) == inv                  # LSE rows overlap
+    assert fwd_ex(L, problem(N=2**20, q=fa.Layout(0, 0, 4096))) == inv        # head past 32-bit offsets
+    assert fwd_ex(L, problem(cu=FAKE, total=0)) == inv                        # packed, no token count
+    assert fwd_ex(L, problem(cu=FAKE + 2, total=10)) == inv                   # misaligned offsets
+    assert fwd_ex(L, problem(), scale=0.0) == inv
+    assert fwd_ex(L, problem(), p=1.0) == inv
+    assert fwd_ex(L, problem(), lse=FAKE + 2) == inv                          # fp32 LSE misaligned
+
+
+def test_ex_accepts_valid_layouts_on_the_host(L):
+    """Every check above passes for these; the calls then stop at the launch,
+    which needs a GPU, so only the validation result is compared."""
+    for d in (32, 64, 96, 128, 256):
+        pb = problem(d=d)
+        assert L.fa_bwd_ex_workspace_size(ctypes.byref(pb)) > 0
+    N, H, d = 100, 3, 64
+    bshd = fa.Layout(N * H * d, d, H * d)
+    pb = problem(q=bshd, k=bshd, v=bshd, o=bshd)
+    assert L.fa_bwd_ex_workspace_size(ctypes.byref(pb)) > 0
+
+
+def test_bwd_ex_workspace(L):
+    inv = fa.FA_ERR_INVALID_ARG
+    rnd = lambda x: (x + 255) // 256 * 256
+    for d, dc in ((32, 64), (64, 64), (96, 128), (128, 128), (256, 256)):
+        pb = problem(B=2, H=3, N=100, d=d)
+        rows = 2 * 3 * 100
+        assert L.fa_bwd_ex_workspace_size(ctypes.byref(pb)) == rnd(rows * dc * 4) + 2 * rnd(rows * 4)
+    pb = problem()
+    assert bwd_ex(L, pb, ws_bytes=1) == inv
+    assert bwd_ex(L, pb, ws=None) == inv
+    assert bwd_ex(L, pb, ws=FAKE * 16 + 8) == inv
+    assert bwd_ex(L, problem(dq=fa.Layout(0, 0, 8))) == inv                   # dq rows overlap
+    assert L.fa_bwd_ex_workspace_size(None) == 0
