@@ -42,12 +42,35 @@ FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd.hip", "exact_io_aware_53_amd/c
                "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
 
 
+DECODE_SOURCES = ["exact_io_aware_53_amd/csrc/fa_decode_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp",
+                  "exact_io_aware_53_amd/csrc/fa_tiles.hpp", "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _profile_value(path, key, sources):
+    if not os.path.exists(path):
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", open(path).read(), flags=re.M))
+    if fields.get("source_hash") != source_hash(sources):
+        return None
+    try:
+        return float(fields[key])
+    except (KeyError, ValueError):
+        return None
+
+
+def decode_traffic(workload_name):
+    """HBM bytes per decode call (split + merge passes) from the committed counter
+    summary, or None when absent or the decode source changed since."""
+    return _profile_value(os.path.join(ROOT, "profiles", f"fa_decode_{workload_name}_counters.md"),
+                          "hbm_bytes_per_call", DECODE_SOURCES)
 
 
 def counter_traffic(workload_name):
@@ -308,7 +331,7 @@ def main():
             dec.append({"workload": wd.name, "ms": round(dms, 4),
                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                     "traffic": None, "ideal_io_bytes": wd.io_bytes()}})
+                                     "traffic": decode_traffic(wd.name), "ideal_io_bytes": wd.io_bytes()}})
             del td, od, ld, wsd
         line["decode"] = dec
 

@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
 
     const int kw = j0 + wave * 32;     // first key of this wave
     const int my_key = kw + l32;
+    // Dropout generator of this lane's key column (counter b, h, row, key).
+    const PhiloxCol philox_col((uint32_t)b, (uint32_t)h, (uint32_t)my_key, p.key);
 
     // Per-lane LDS byte offsets of the operand reads. The chunk swizzle depends
     // only on the low four row bits, so the 16-row and 32-row block terms added
@@ -341,8 +343,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                     const float pr = fast_exp2(s[qb][r]);     // exp2(-inf) = 0
                     float z = 1.0f;
                     if (DROPOUT) {
-                        const uint32_t w = philox_word0((uint32_t)b, (uint32_t)h, (uint32_t)qi,
-                                                        (uint32_t)my_key, p.key);
+                        const uint32_t w = philox_col.word0((uint32_t)qi);
                         z = w >= p.thr ? p.inv_keep : 0.0f;
                     }
                     const float ds = pr * fmaf(dp[qb][r], z, -dsum_t[qrow]);

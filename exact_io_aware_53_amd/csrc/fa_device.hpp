@@ -242,4 +242,46 @@ struct PhiloxRow {
     }
 };
 
+// Word 0 at counter (c0, c1, i, c3) for a fixed (c0, c1, c3) and varying row
+// i (the key-side backward: a lane holds one key j = c3 against many rows):
+//   round 1: x2 = hi(M0 c0) ^ c3 ^ k1 and x3 = lo(M0 c0) fixed; x0, x1 from M1 i
+//   round 2: y1 = lo(M1 x2) and hi(M1 x2) ^ k0 fixed; y0, y2, y3 vary
+struct PhiloxCol {
+    uint32_t c1k0, G, y1, X3K;   // c1 ^ k0 (round 1); hi(M1 x2) ^ k0 and lo(M1 x2), x3 ^ k1 (round 2)
+    uint32_t k0_2, k1_2;          // key of round 3
+
+    PhiloxCol() = default;
+    __device__ __forceinline__ PhiloxCol(uint32_t c0, uint32_t c1, uint32_t c3, PhiloxKey key) {
+        uint32_t k0 = key.k0, k1 = key.k1;
+        const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;   // round 1, fixed half
+        const uint32_t x2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t x3 = (uint32_t)p0;
+        c1k0 = c1 ^ k0;
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+        const uint64_t q1 = (uint64_t)kPhiloxM1 * x2;   // round 2, fixed half
+        G = (uint32_t)(q1 >> 32) ^ k0;
+        y1 = (uint32_t)q1;
+        X3K = x3 ^ k1;
+        k0_2 = k0 + kPhiloxW0;
+        k1_2 = k1 + kPhiloxW1;
+    }
+
+    __device__ __forceinline__ uint32_t word0(uint32_t i) const {
+        const uint64_t p1 = (uint64_t)kPhiloxM1 * i;          // round 1, varying half
+        const uint32_t x0 = (uint32_t)(p1 >> 32) ^ c1k0;
+        const uint32_t x1 = (uint32_t)p1;
+        const uint64_t q0 = (uint64_t)kPhiloxM0 * x0;         // round 2, varying half
+        uint32_t c0 = G ^ x1, c1 = y1, c2 = (uint32_t)(q0 >> 32) ^ X3K, c3 = (uint32_t)q0;
+        uint32_t k0 = k0_2, k1 = k1_2;
+#pragma unroll
+        for (int r = 2; r < 9; ++r) {
+            philox_round(c0, c1, c2, c3, k0, k1);
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        return xor3((uint32_t)(((uint64_t)kPhiloxM1 * c2) >> 32), c1, k0);
+    }
+};
+
 }  // namespace fa
