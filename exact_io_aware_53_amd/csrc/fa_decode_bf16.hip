@@ -324,10 +324,16 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Workgroups the key split aims at: two per CU, all resident at once (one
+// round). Measured on the decode workloads: 256 and 512 stream at 70-74% of
+// 8 TB/s, 1024 at 64-70%, 4096 at 48-64% (more partial results, more merge).
+#ifndef FA_DEC_TARGET
+#define FA_DEC_TARGET 512
+#endif
+
 DecodeSplit decode_split(int B, int H, int Nq, int Nk) {
-    // Enough workgroups for two rounds over the 256 CUs (two per CU resident),
-    // chunks of whole 128-key steps.
-    constexpr long long kTargetWorkgroups = 1024;
+    // Chunks of whole 128-key steps.
+    constexpr long long kTargetWorkgroups = FA_DEC_TARGET;
     DecodeSplit sp;
     sp.nrb = (Nq + 31) / 32;
     const long long base = (long long)B * H * sp.nrb;
