@@ -295,13 +295,4 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
     return a.s.d == 64 ? bwd_simple<float, 64>(a, st) : bwd_simple<float, 128>(a, st);
 }
 
-// bf16 storage through the same fp32 arithmetic.
-hipError_t launch_bwd_bf16_simple(const BwdArgs& a, hipStream_t st) {
-    return a.s.d == 64 ? bwd_simple<__bf16, 64>(a, st) : bwd_simple<__bf16, 128>(a, st);
-}
-
-hipError_t launch_fwd_bf16_simple(const FwdArgs& a, hipStream_t st) {
-    return a.s.d == 64 ? fwd_simple<__bf16, 64>(a, st) : fwd_simple<__bf16, 128>(a, st);
-}
-
 }  // namespace fa
