@@ -47,6 +47,10 @@
 namespace fa {
 namespace {
 
+// Key-side two-pass kernel at d = 128: dK^T and dV^T accumulate in AGPRs.
+#ifndef FA_KV_AGPR
+#define FA_KV_AGPR 1
+#endif
 #ifndef FA_KV_PF
 #define FA_KV_PF 2
 #endif
@@ -118,6 +122,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
     // LDS operand pairs in flight ahead of their products (S/dP, then dV/dK).
     constexpr int kPf = D == 256 ? 1 : FA_KV_PF, kTf = D == 256 ? 1 : FA_KV_TF;
+    // d = 128, two-pass form: dK^T and dV^T accumulate in AGPRs through inline
+    // products, leaving the VGPRs to K, V, the score tile and the operand rings.
+    constexpr bool kAgpr = FA_KV_AGPR && D == 128 && !DQ;
     __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char k_s[DQ ? kBKV * D * 2 : 16];
@@ -263,10 +270,10 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
         const float* const lse_t = lse_s + buf * 64;
         const float* const dsum_t = dsum_s + buf * 64;
 
-        // Every query of the tile precedes our keys. (d = 256 runs such tiles fully
-        // masked instead: their zero contributions cost less than the register
-        // shuffling a second path through the loop costs at 512 registers.)
-        const bool skip = CAUSAL && D != 256 && kw > i0 + BQ - 1;
+        // Every query of the tile precedes our keys. (d = 256, and dK/dV in AGPRs,
+        // run such tiles fully masked instead: their zero contributions cost
+        // less than the register copies a second path through the loop costs.)
+        const bool skip = CAUSAL && D != 256 && !kAgpr && kw > i0 + BQ - 1;
         if (skip) {
             // this wave's rows of dS^T are zero for this tile
             if constexpr (DQ)
@@ -388,8 +395,13 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                             bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
                         }
                     }
-                    dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
-                    dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
+                    if constexpr (kAgpr) {
+                        mfma_agpr(dva[db], oa[j % kTf], bp);
+                        mfma_agpr(dka[db], ta[j % kTf], bs);
+                    } else {
+                        dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
+                        dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
+                    }
                     if (j + kTf < TI) {
                         oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
                         ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
@@ -434,6 +446,13 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     }
 
     // dK = s dK^T, dV = dV^T, transposed on the way out (lane = key, registers = d)
+    if constexpr (kAgpr) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            settle(dka[db]);
+            settle(dva[db]);
+        }
+    }
     if (my_key < N) {
         T* dkr = (T*)p.dk + p.ldk.base(b, h, start) + (size_t)my_key * p.ldk.sn;
         T* dvr = (T*)p.dv + p.ldv.base(b, h, start) + (size_t)my_key * p.ldv.sn;
