@@ -97,11 +97,37 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, FA_LD
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_wave_base, 16, voffset, 0, 0, 0);
 }
 
+// The same copy issued as inline assembly, outside the compiler's wait-count
+// tracking. The compiler cannot tell which LDS buffer a copy writes, so it
+// makes every later LDS read wait for every copy still in flight, and a
+// double-buffered loop that issues the next tile's copy before reading the
+// current tile would wait for that copy first. Callers of this form order it
+// themselves: s_waitcnt vmcnt(0) (wait_vmem) and a workgroup barrier before any
+// read of the destination, and no write of the destination's LDS by other code
+// while it may be in flight. It has no register outputs; M0 carries the wave's
+// LDS base, written by the compiler (the copy leads with the one wait state
+// it needs after an M0 write).
+__device__ __forceinline__ void buffer_to_lds16_async(__amdgpu_buffer_rsrc_t rs, FA_LDS void* lds_wave_base,
+                                                      uint32_t voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "{m0}"(m0), "v"(voffset), "s"(rs)
+                 : "memory");
+}
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voffset) {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin
+// so that the compiler's own wait tracking sees its loads complete here; an
+// asm form would leave the compiler waiting for them again later, by counts
+// that the untracked copies above would then stretch.
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // ------------------------------------------------------------- LDS swizzle
 // gfx950 LDS serves 256 bytes per pass: 16 lanes of a 16-byte read, or 32

@@ -62,8 +62,9 @@ struct TileCopy {
         const uint32_t toff = __builtin_amdgcn_readfirstlane((uint32_t)t * step);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            // blocks i * NW + wave with i < PER - 1 are below BLKS for every wave
             const int blk = i * NW + wave;
-            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), off[i] + toff);
+            if (i < PER - 1 || blk < BLKS) buffer_to_lds16_async(rs, (FA_LDS void*)(base + blk * 1024), off[i] + toff);
         }
     }
 };
