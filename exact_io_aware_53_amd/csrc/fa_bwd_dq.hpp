@@ -84,7 +84,8 @@ struct SwizzledCopy {
             // Padded chunks keep their out-of-range offset (no tile offset added,
             // so it cannot wrap back into range).
             const uint32_t o = DH == D || off[i] != 0xf0000000u ? off[i] + toff : off[i];
-            if (blk < BLKS) buffer_to_lds16(rs, (FA_LDS void*)(base + blk * 1024), o);
+            // blocks i * NW + wave with i < PER - 1 are below BLKS for every wave
+            if (i < PER - 1 || blk < BLKS) buffer_to_lds16_async(rs, (FA_LDS void*)(base + blk * 1024), o);
         }
     }
 };

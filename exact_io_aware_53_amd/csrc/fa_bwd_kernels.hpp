@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
         for (int i = 0; i < KLOADS; ++i) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
-            buffer_to_lds16(rs_k, (FA_LDS void*)(kL + blk * 1024),
+            buffer_to_lds16_async(rs_k, (FA_LDS void*)(kL + blk * 1024),
                             chunk_src<DH>(j0 + row, sw ^ chunk_swizzle<CH>(row), ldk));
         }
     }
@@ -234,15 +234,11 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
             const int blk = i * kNW + wave, pos = blk * 64 + lane;
             const int row = pos / CH, sw = pos % CH;
             const int ch = sw ^ chunk_swizzle<CH>(row);
-            buffer_to_lds16(rs_q, (FA_LDS void*)(qL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldq));
-            buffer_to_lds16(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldo));
+            buffer_to_lds16_async(rs_q, (FA_LDS void*)(qL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldq));
+            buffer_to_lds16_async(rs_do, (FA_LDS void*)(doL + buf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldo));
         }
-        if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lse, (FA_LDS void*)(lse_s + buf * 64), 4,
-                                                     (uint32_t)(i0 + lane) * 4, 0, 0, 0);
-        if (wave == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_ds, (FA_LDS void*)(dsum_s + buf * 64), 4,
-                                                     (uint32_t)(i0 + lane) * 4, 0, 0, 0);
+        if (wave == 0) buffer_to_lds4_async(rs_lse, (FA_LDS void*)(lse_s + buf * 64), (uint32_t)(i0 + lane) * 4);
+        if (wave == 1) buffer_to_lds4_async(rs_ds, (FA_LDS void*)(dsum_s + buf * 64), (uint32_t)(i0 + lane) * 4);
     };
 
     // Query tiles run from the last one down to the first one this key block

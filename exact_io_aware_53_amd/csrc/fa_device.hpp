@@ -105,12 +105,25 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, FA_LD
 // themselves: s_waitcnt vmcnt(0) (wait_vmem) and a workgroup barrier before any
 // read of the destination, and no write of the destination's LDS by other code
 // while it may be in flight. It has no register outputs; M0 carries the wave's
-// LDS base, written by the compiler (the copy leads with the one wait state
-// it needs after an M0 write).
+// LDS base, written by the compiler. The compiler's hazard checks do not see
+// into the asm, so it leads with the five wait states a vector-memory
+// instruction needs after a vector instruction wrote one of the SGPRs it reads
+// (v_readlane / v_readfirstlane into the resource words or M0, as SGPR spills
+// and reloads produce); that also covers the one wait state after an M0 write.
 __device__ __forceinline__ void buffer_to_lds16_async(__amdgpu_buffer_rsrc_t rs, FA_LDS void* lds_wave_base,
                                                       uint32_t voffset) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "{m0}"(m0), "v"(voffset), "s"(rs)
+                 : "memory");
+}
+
+// 4 bytes per lane into LDS at lds_wave_base + lane * 4, ordered the same way.
+__device__ __forceinline__ void buffer_to_lds4_async(__amdgpu_buffer_rsrc_t rs, FA_LDS void* lds_wave_base,
+                                                     uint32_t voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :
                  : "{m0}"(m0), "v"(voffset), "s"(rs)
                  : "memory");
