@@ -8,7 +8,8 @@ forward (B=2, H=32, N=8192, d=128, Q scaled by 4). The same JSON line also
 carries the forward+backward measurement on the dropout workload
 (B=2, H=16, N=4096, d=64, p=0.1; the backward in both its fused atomic form
 and its two-pass deterministic form), the backward at the default workload's
-shape, the long-context forward (B=1, H=16, N=32768, d=128) with an N sweep
+shape, the fp32 B1 H1 N128 d64 and bf16 causal B4 H16 N2048 d64 forwards
+(`other_configs`), the long-context forward (B=1, H=16, N=32768, d=128) with an N sweep
 and the device memory each call takes, the decode-shaped forward on its three workloads (HBM-bound: GB/s
 against 8 TB/s), the general entry points on head sizes 32/96/256, fp16,
 [B, N, H, d] storage and a packed variable-length batch (`coverage`), the
@@ -147,6 +148,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fwd-bwd", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the fp32 B1 H1 N128 and bf16 B4 H16 N2048 d64 forward timings")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context forward and its N sweep")
     ap.add_argument("--no-coverage", action="store_true",
                     help="skip the head-size / fp16 / layout / packed-batch measurements")
@@ -305,6 +308,28 @@ def main():
             torch.cuda.empty_cache()
         line["long_context"] = {"workload": wl.name, "sweep": sweep,
                                 "s_matrix_bytes_avoided_bf16": 2 * wl.B * wl.H * wl.N * wl.N}
+
+    if not args.no_other:
+        # The two remaining forward configurations: the fp32 B1 H1 N128 d64
+        # non-causal forward (launch-bound: microseconds are what it shows) and
+        # the causal bf16 B4 H16 N2048 d64 forward.
+        others = []
+        for name in ("fwd_f32_b1h1n128d64", "fwd_causal_bf16_b4h16n2048d64"):
+            wo = WORKLOADS[name]
+            ho = make_inputs(wo, with_grad_out=False)
+            qo, ko, vo = (ho[x].to(dev) for x in ("q", "k", "v"))
+            oo = torch.empty_like(qo)
+            lo = torch.empty((wo.B, wo.H, wo.N), dtype=torch.float32, device=dev)
+
+            def fo():
+                fa.fwd(qo, ko, vo, scale=wo.scale, causal=wo.causal, out=oo, lse=lo)
+
+            _, evo = time_launches(fo, args.steps, args.warmup, stream)
+            mo = sum(evo) / len(evo)
+            others.append({"workload": name, "dtype": wo.dtype, "us": round(mo * 1e3, 2),
+                           "tflops": round(wo.fwd_flops() / (mo * 1e-3) / 1e12, 3)})
+            del qo, ko, vo, oo, lo
+        line["other_configs"] = others
 
     if not args.no_decode:
         from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs

@@ -91,20 +91,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// 16 bytes per lane from the buffer into LDS at lds_wave_base + lane * 16.
-__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, FA_LDS void* lds_wave_base,
-                                                uint32_t voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_wave_base, 16, voffset, 0, 0, 0);
-}
-
-// The same copy issued as inline assembly, outside the compiler's wait-count
-// tracking. The compiler cannot tell which LDS buffer a copy writes, so it
-// makes every later LDS read wait for every copy still in flight, and a
-// double-buffered loop that issues the next tile's copy before reading the
-// current tile would wait for that copy first. Callers of this form order it
-// themselves: s_waitcnt vmcnt(0) (wait_vmem) and a workgroup barrier before any
-// read of the destination, and no write of the destination's LDS by other code
-// while it may be in flight. It has no register outputs; M0 carries the wave's
+// 16 bytes per lane from the buffer into LDS at lds_wave_base + lane * 16,
+// issued as inline assembly, outside the compiler's wait-count tracking. With
+// the compiler's own LDS-copy builtin the compiler cannot tell which LDS
+// buffer a copy writes, so it makes every later LDS read wait for every copy
+// still in flight, and a double-buffered loop that issues the next tile's
+// copy before reading the current tile would wait for that copy first.
+// Callers order it themselves: s_waitcnt vmcnt(0) (wait_vmem) and a workgroup
+// barrier before any read of the destination, and no write of the
+// destination's LDS by other code while it may be in flight. It has no register outputs; M0 carries the wave's
 // LDS base, written by the compiler. The compiler's hazard checks do not see
 // into the asm, so it leads with the five wait states a vector-memory
 // instruction needs after a vector instruction wrote one of the SGPRs it reads
