@@ -3,7 +3,7 @@
 // matrix cores' bf16 path does not apply.
 //
 // Forward: the tile-by-tile method of "DL0056 FlashAttention" (intvml),
-// "Mathematical Formulation": each workgroup owns 64 query rows, streams K/V
+// "Mathematical Formulation": each workgroup owns 16 query rows, streams K/V
 // tiles of 32 keys through LDS, keeps the running row maximum m and the
 // rescaled running denominator l, and rescales its output accumulator by the
 // same factor exp(m_old - m_new) (the output update the page describes in
@@ -22,9 +22,9 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;      // query (forward, dQ) or key (dK/dV) rows per workgroup
+constexpr int kRows = 64;      // backward: query (dQ) or key (dK/dV) rows per workgroup
 constexpr int kTile = 32;      // streamed rows per LDS tile
-constexpr int kThreads = 256;  // 4 threads per row, each owning d/4 columns
+constexpr int kThreads = 256;  // backward: 4 threads per row, each owning d/4 columns
 
 template <typename T> __device__ __forceinline__ float ld(const T* p) { return (float)*p; }
 template <typename T> __device__ __forceinline__ void st(T* p, float x) { *p = (T)x; }
@@ -60,27 +60,42 @@ __device__ __forceinline__ void stage_rows(float (*dst)[D], const T* src, int r0
     }
 }
 
+// Forward: 16 query rows per workgroup, 16 consecutive lanes per row, each
+// lane owning D/16 columns. For a 32-key tile a lane first forms its partial
+// dot products with all 32 keys (independent chains), then each is summed over
+// the row's 16 lanes.
+constexpr int kFRows = 16;
+constexpr int kFLanes = kThreads / kFRows;
+
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
-    constexpr int DQ = D / 4;
+    constexpr int DC = D / kFLanes;
     __shared__ float ks[kTile][D];
     __shared__ float vs[kTile][D];
-    const int nblk = (p.N + kRows - 1) / kRows;
+    const int nblk = (p.N + kFRows - 1) / kFRows;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int b = bh / p.H, h = bh % p.H;
-    const int row = blk * kRows + threadIdx.x / 4, c0 = (threadIdx.x % 4) * DQ;
+    const int row = blk * kFRows + threadIdx.x / kFLanes, c0 = (threadIdx.x % kFLanes) * DC;
     const size_t head = (size_t)bh * p.N * D;
     const T* q = (const T*)p.q + head;
     const T* k = (const T*)p.k + head;
     const T* v = (const T*)p.v + head;
 
-    float qr[DQ], acc[DQ];
-    for (int t = 0; t < DQ; ++t) {
+    float qr[DC], acc[DC];
+    for (int t = 0; t < DC; ++t) {
         qr[t] = row < p.N ? ld(q + (size_t)row * D + c0 + t) : 0.0f;
         acc[t] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
-    const int last_row = min(p.N, (blk + 1) * kRows) - 1;
+    const int last_row = min(p.N, (blk + 1) * kFRows) - 1;
     const int key_end = p.causal ? last_row + 1 : p.N;
     for (int k0 = 0; k0 < key_end; k0 += kTile) {
         __syncthreads();
@@ -88,11 +103,17 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
         stage_rows<T, D>(vs, v, k0, p.N);
         __syncthreads();
         float s[kTile];
-        float tmax = -INFINITY;
+#pragma unroll
         for (int j = 0; j < kTile; ++j) {
             float part = 0.0f;
-            for (int t = 0; t < DQ; ++t) part = fmaf(qr[t], ks[j][c0 + t], part);
-            const float sc = quad_sum(part) * p.scale;
+#pragma unroll
+            for (int t = 0; t < DC; ++t) part = fmaf(qr[t], ks[j][c0 + t], part);
+            s[j] = part;
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kTile; ++j) {
+            const float sc = row_sum16(s[j]) * p.scale;
             const int key = k0 + j;
             const bool live = key < p.N && (!p.causal || key <= row);
             s[j] = live ? sc : -INFINITY;
@@ -102,12 +123,14 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
         if (m_new == -INFINITY) continue;          // nothing visible yet for this row
         const float alpha = expf(m - m_new);       // 0 on the first live tile
         float psum = 0.0f;
-        for (int t = 0; t < DQ; ++t) acc[t] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DC; ++t) acc[t] *= alpha;
         for (int j = 0; j < kTile; ++j) {
             const float pj = expf(s[j] - m_new);   // exp(-inf) = 0 for masked keys
             psum += pj;
             const float w = pj * keep_scale(p, b, h, row, k0 + j);
-            for (int t = 0; t < DQ; ++t) acc[t] = fmaf(w, vs[j][c0 + t], acc[t]);
+#pragma unroll
+            for (int t = 0; t < DC; ++t) acc[t] = fmaf(w, vs[j][c0 + t], acc[t]);
         }
         l = alpha * l + psum;
         m = m_new;
@@ -115,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
     if (row < p.N) {
         const float inv = 1.0f / l;
         T* o = (T*)p.out0 + head + (size_t)row * D + c0;
-        for (int t = 0; t < DQ; ++t) st(o + t, acc[t] * inv);
-        if (threadIdx.x % 4 == 0) p.lse_out[(size_t)bh * p.N + row] = m + logf(l);
+        for (int t = 0; t < DC; ++t) st(o + t, acc[t] * inv);
+        if (threadIdx.x % kFLanes == 0) p.lse_out[(size_t)bh * p.N + row] = m + logf(l);
     }
 }
 
@@ -266,7 +289,7 @@ template <typename T, int D>
 hipError_t fwd_simple(const FwdArgs& a, hipStream_t st) {
     SimpleParams p = make_params(a.s);
     p.q = a.q; p.k = a.k; p.v = a.v; p.out0 = a.o; p.lse_out = a.lse;
-    const int nblk = (a.s.N + kRows - 1) / kRows;
+    const int nblk = (a.s.N + kFRows - 1) / kFRows;
     hipLaunchKernelGGL((fwd_simple_kernel<T, D>), dim3(a.s.B * a.s.H * nblk), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
