@@ -29,7 +29,7 @@
 namespace fa {
 namespace {
 
-constexpr float DEC_SLACK = 8.0f;   // lazy rescale slack (log2 units), as in the forward
+constexpr float DEC_SLACK = 8.0f;   // lazy rescale slack (log2 units), as in the forward with dropout
 constexpr int kDecNW = 4;           // waves per workgroup
 constexpr int kDecTile = 32;        // keys per wave tile
 constexpr int kDecChunk = kDecNW * kDecTile;   // key chunks are multiples of this

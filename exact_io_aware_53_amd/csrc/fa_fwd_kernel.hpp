@@ -50,14 +50,24 @@
 namespace fa {
 namespace {
 
-// Slack, in log2 units, by which a tile maximum may exceed the reference
-// maximum m2 before O~ and l are rescaled to it. Until then the exponentials
-// are taken against the stale reference: P~ <= 2^RESCALE_SLACK, and every
-// factor cancels in O~ / l, so the result is exact. To keep the dominant term
-// of a peaked row free of bf16 rounding error, O~ is normalised by the sum of
-// the same bf16-rounded weights it accumulated (lb); the fp32 sum (l) gives
-// the log-sum-exp.
-constexpr float RESCALE_SLACK = 8.0f;
+// Without dropout, the exponentials of a tile are taken against the reference
+// maximum m2 of the tiles before it, without first finding the tile's own
+// maximum: every factor exp2(m2) cancels in O~ / l, so the result does not
+// depend on which reference is used as long as nothing overflows. The fp32 row
+// sum l, which the softmax forms anyway, watches for that: once a lane's share
+// of l reaches SUM_LIMIT (or is inf / NaN, as on the first tile, where
+// m2 = -inf), the tile is redone from its scores against the true running
+// maximum, with l, lb and O~ rescaled to it. Weights therefore stay below 2^20
+// and sums below 2^21, far inside fp32 and bf16 range, and the common path
+// spends no instructions on the row maximum. With dropout the scores cannot
+// stay live for a second pass without spilling (the generator needs the
+// registers), so those kernels find the maximum first and move the reference
+// once it is exceeded by DROPOUT_SLACK. To keep the dominant term of a peaked
+// row free of bf16 rounding error, O~ is normalised by the sum of the same
+// bf16-rounded weights it accumulated (lb); the fp32 sum (l) gives the
+// log-sum-exp.
+constexpr float SUM_LIMIT = 1048576.0f;   // 2^20
+constexpr float DROPOUT_SLACK = 8.0f;     // log2 units
 
 // LDS operand reads kept in flight ahead of the matrix-core product that uses them.
 #ifndef FA_FWD_PREFETCH
@@ -260,26 +270,61 @@ void fwd_kernel(FwdParams p) {
                             s[rb][kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[rb][kb][r];
                 }
 
-                // ---- online softmax (log2 domain)
-                float mx = -INFINITY;
+                // ---- online softmax (log2 domain): P~ = exp2(s c - m2) into pb,
+                // adding to this lane's shares of l and lb
+                const V2 ones = {(T)1.0f, (T)1.0f};
+                auto weights = [&](const uint32_t* keep) {
+                    const float neg = -m2[rb];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
-                mx = max_with_partner32(mx) * p.sl2;
-                if (__builtin_amdgcn_ballot_w64(mx > m2[rb] + RESCALE_SLACK)) {
+                        for (int r = 0; r < 16; r += 2) {
+                            const float x0 = fast_exp2(fmaf(s[rb][kb][r], p.sl2, neg));
+                            const float x1 = fast_exp2(fmaf(s[rb][kb][r + 1], p.sl2, neg));
+                            lsum[rb] += x0;
+                            lsum[rb] += x1;
+                            V2 w;
+                            w[0] = (T)x0;
+                            w[1] = (T)x1;
+                            lbf[rb] = dot2(w, ones, lbf[rb]);
+                            if (DROPOUT) {
+                                w[0] = (T)((keep[kb] >> r) & 1u ? x0 : 0.0f);
+                                w[1] = (T)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
+                            }
+                            const int pc = kb * 2 + r / 8, pi = r % 8;
+                            pb[rb][pc][pi] = w[0];
+                            pb[rb][pc][pi + 1] = w[1];
+                        }
+                };
+                // move the reference to the running maximum, rescaling l, lb and O~
+                auto to_max = [&](float l0, float lb0) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+                    mx = max_with_partner32(mx) * p.sl2;
                     const float m_new = fmaxf(m2[rb], mx);
-                    const float alpha = fast_exp2(m2[rb] - m_new);   // exp2(-inf) = 0 on the first tile
-                    lsum[rb] *= alpha;
-                    lbf[rb] *= alpha;
+                    // exp2(-inf) = 0 when the row had no reference yet; a row with no
+                    // visible key so far keeps factor 1
+                    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m2[rb] - m_new);
+                    lsum[rb] = l0 * alpha;
+                    lbf[rb] = lb0 * alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
                     m2[rb] = m_new;
-                }
-                uint32_t keep[KB];
-                if (DROPOUT) {
+                };
+                if constexpr (DROPOUT) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+                    if (__builtin_amdgcn_ballot_w64(max_with_partner32(mx) * p.sl2 > m2[rb] + DROPOUT_SLACK))
+                        to_max(lsum[rb], lbf[rb]);
+                    uint32_t keep[KB];
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
                         uint32_t bits = 0;
@@ -290,29 +335,16 @@ void fwd_kernel(FwdParams p) {
                         }
                         keep[kb] = bits;
                     }
-                }
-                const float neg = -m2[rb];
-                const V2 ones = {(T)1.0f, (T)1.0f};
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const float x0 = fast_exp2(fmaf(s[rb][kb][r], p.sl2, neg));
-                        const float x1 = fast_exp2(fmaf(s[rb][kb][r + 1], p.sl2, neg));
-                        lsum[rb] += x0;
-                        lsum[rb] += x1;
-                        V2 w;
-                        w[0] = (T)x0;
-                        w[1] = (T)x1;
-                        lbf[rb] = dot2(w, ones, lbf[rb]);
-                        if (DROPOUT) {
-                            w[0] = (T)((keep[kb] >> r) & 1u ? x0 : 0.0f);
-                            w[1] = (T)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
-                        }
-                        const int pc = kb * 2 + r / 8, pi = r % 8;
-                        pb[rb][pc][pi] = w[0];
-                        pb[rb][pc][pi + 1] = w[1];
+                    weights(keep);
+                } else {
+                    const float l0 = lsum[rb], lb0 = lbf[rb];
+                    weights(nullptr);
+                    if (__builtin_amdgcn_ballot_w64(!(lsum[rb] < SUM_LIMIT))) {
+                        // a weight outgrew the reference: redo the tile against the maximum
+                        to_max(l0, lb0);
+                        weights(nullptr);
                     }
+                }
             }
 
             // ---- O~^T += V^T P^T; each V^T operand read feeds the RB row blocks
