@@ -297,6 +297,23 @@ def test_uniform_scores_and_causal_row0_on_gpu():
     assert torch.equal(o2[0, 0, 0].cpu(), v[0, 0, 0])
 
 
+@pytest.mark.parametrize("p", [0.0, 0.1])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_wide_score_range(d, causal, p):
+    """Q scaled by 16 (exact in bf16): scores spread over tens of log2 units, so a
+    row's maximum jumps between key tiles, weights taken against the reference
+    maximum of earlier tiles overflow fp32, and the forward's rescale path runs on
+    most rows of most tiles. O and LSE still match the oracle on every row."""
+    B, H, N = 1, 2, 700
+    q, k, v = normal_tensors((B, H, N, d), 7331 + d, 3, torch.bfloat16)
+    q = (q.float() * 16.0).to(torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=p, seed=SEED)
+    torch.cuda.synchronize()
+    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL["bf16"], [(0, 0), (0, 1)],
+                        tag=f"d={d} causal={causal} p={p}")
+
+
 def test_forward_takes_no_device_memory_and_inputs_grow_linearly():
     """The forward needs no workspace: with outputs preallocated, free device
     memory is the same before and after a call at every N; the tensors a call
