@@ -317,60 +317,39 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
+            // P and dS of 16-row chunk qc + 1 between the dV/dK products of chunk qc
+            // (the two-pass form at d = 64: one wave per SIMD, so no other wave fills
+            // the matrix core while this one does vector work; measured 4% faster).
+            // At d = 128 it measured no faster, and the padded d = 32 kernel would
+            // lose a wave per SIMD, so every other kernel keeps the order below.
+            constexpr bool kChunked = !DQ && D == 64 && DH == 64;
+            if constexpr (kChunked) {
+                if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
+                    const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
+                    const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+                    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[qb][r] = fmaf(s[qb][r], p.sl2, -lse_t[qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)]);
-            // Only tiles that cross the diagonal or a ragged end hold masked elements.
-            // Element (qb, r) is query row i0 + 4hi + e with e = 32qb + 8(r/4) + r%4, a
-            // compile-time offset; the bounds are moved to the lane's side.
-            if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
-                const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
-                const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int e = qb * 32 + 8 * (r >> 2) + (r & 3);
-                        if (e < e_lo || e >= e_hi) s[qb][r] = -INFINITY;
-                    }
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                        for (int r = 0; r < 16; ++r) {
+                            const int e = qb * 32 + 8 * (r >> 2) + (r & 3);
+                            if (e < e_lo || e >= e_hi) s[qb][r] = -INFINITY;   // -inf stays -inf below
+                        }
+                }
+                // P = exp2(s scale log2(e) - LSE_i log2(e)) and dS = P (dP Z' - D_i) of
+                // element (qb, r), rounded to the element type into the product
+                // operands bp_out[idx] (P Z', for dV) and bs_out[idx] (dS, for dK)
+                auto p_ds = [&](int qb, int r, V8& bp_out, V8& bs_out, int idx) {
                     const int qrow = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const int qi = i0 + qrow;
-                    const float pr = fast_exp2(s[qb][r]);     // exp2(-inf) = 0
+                    const float pr = fast_exp2(fmaf(s[qb][r], p.sl2, -lse_t[qrow]));   // exp2(-inf) = 0
                     float z = 1.0f;
                     if (DROPOUT) {
-                        const uint32_t w = philox_col.word0((uint32_t)qi);
+                        const uint32_t w = philox_col.word0((uint32_t)(i0 + qrow));
                         z = w >= p.thr ? p.inv_keep : 0.0f;
                     }
                     const float ds = pr * fmaf(dp[qb][r], z, -dsum_t[qrow]);
-                    s[qb][r] = pr * z;      // P Z' for dV
-                    dp[qb][r] = ds;         // dS
-                }
-            // dV^T += dO^T (P Z'),  dK^T += Q^T dS  (contraction over the tile's query rows)
-            if constexpr (DQ) {
-#pragma unroll
-                for (int qc = 0; qc < BQ / 16; ++qc) {
-                    V8 bp, bs;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
-                        bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
-                    }
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
-                        dva[db] = mfma32(tr_read<V8>(doT, o0, o1), bp, dva[db]);
-                        dka[db] = mfma32(tr_read<V8>(qT, o0, o1), bs, dka[db]);
-                    }
-                }
-            } else {
+                    bp_out[idx] = (T)(pr * z);
+                    bs_out[idx] = (T)ds;
+                };
                 constexpr int TI = (BQ / 16) * DB;     // steps j = qc * DB + db
                 auto to = [&](int j, int half) { return troff[j % DB][half] + 16 * (j / DB) * ROW; };
                 V8 oa[kTf], ta[kTf];
@@ -379,30 +358,121 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                     oa[j] = tr_read<V8>(doT, to(j, 0), to(j, 1));
                     ta[j] = tr_read<V8>(qT, to(j, 0), to(j, 1));
                 }
+                V8 bp[2], bs[2];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) p_ds(0, i, bp[0], bs[0], i);
                 __builtin_amdgcn_sched_barrier(0);
-                V8 bp, bs;
 #pragma unroll
                 for (int j = 0; j < TI; ++j) {
                     const int qc = j / DB, db = j % DB;
-                    if (db == 0) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
-                            bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
-                        }
-                    }
                     if constexpr (kAgpr) {
-                        mfma_agpr(dva[db], oa[j % kTf], bp);
-                        mfma_agpr(dka[db], ta[j % kTf], bs);
+                        mfma_agpr(dva[db], oa[j % kTf], bp[qc & 1]);
+                        mfma_agpr(dka[db], ta[j % kTf], bs[qc & 1]);
                     } else {
-                        dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
-                        dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
+                        dva[db] = mfma32(oa[j % kTf], bp[qc & 1], dva[db]);
+                        dka[db] = mfma32(ta[j % kTf], bs[qc & 1], dka[db]);
                     }
                     if (j + kTf < TI) {
                         oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
                         ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
                     }
+                    // the elements of chunk qc + 1 that ride behind these products
+                    if (qc + 1 < BQ / 16) {
+                        const int nq = qc + 1;
+#pragma unroll
+                        for (int i = db * 8 / DB; i < (db + 1) * 8 / DB; ++i)
+                            p_ds(nq >> 1, 8 * (nq & 1) + i, bp[nq & 1], bs[nq & 1], i);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // log2 of P: s * scale * log2(e) - LSE_i * log2(e)
+    #pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[qb][r] = fmaf(s[qb][r], p.sl2, -lse_t[qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)]);
+                // Only tiles that cross the diagonal or a ragged end hold masked elements.
+                // Element (qb, r) is query row i0 + 4hi + e with e = 32qb + 8(r/4) + r%4, a
+                // compile-time offset; the bounds are moved to the lane's side.
+                if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
+                    const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
+                    const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
+    #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int e = qb * 32 + 8 * (r >> 2) + (r & 3);
+                            if (e < e_lo || e >= e_hi) s[qb][r] = -INFINITY;
+                        }
+                }
+    #pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qrow = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        const int qi = i0 + qrow;
+                        const float pr = fast_exp2(s[qb][r]);     // exp2(-inf) = 0
+                        float z = 1.0f;
+                        if (DROPOUT) {
+                            const uint32_t w = philox_col.word0((uint32_t)qi);
+                            z = w >= p.thr ? p.inv_keep : 0.0f;
+                        }
+                        const float ds = pr * fmaf(dp[qb][r], z, -dsum_t[qrow]);
+                        s[qb][r] = pr * z;      // P Z' for dV
+                        dp[qb][r] = ds;         // dS
+                    }
+                // dV^T += dO^T (P Z'),  dK^T += Q^T dS  (contraction over the tile's query rows)
+                if constexpr (DQ) {
+    #pragma unroll
+                    for (int qc = 0; qc < BQ / 16; ++qc) {
+                        V8 bp, bs;
+    #pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
+                            bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
+                        }
+    #pragma unroll
+                        for (int db = 0; db < DB; ++db) {
+                            const int o0 = troff[db][0] + 16 * qc * ROW, o1 = troff[db][1] + 16 * qc * ROW;
+                            dva[db] = mfma32(tr_read<V8>(doT, o0, o1), bp, dva[db]);
+                            dka[db] = mfma32(tr_read<V8>(qT, o0, o1), bs, dka[db]);
+                        }
+                    }
+                } else {
+                    constexpr int TI = (BQ / 16) * DB;     // steps j = qc * DB + db
+                    auto to = [&](int j, int half) { return troff[j % DB][half] + 16 * (j / DB) * ROW; };
+                    V8 oa[kTf], ta[kTf];
+    #pragma unroll
+                    for (int j = 0; j < kTf; ++j) {
+                        oa[j] = tr_read<V8>(doT, to(j, 0), to(j, 1));
+                        ta[j] = tr_read<V8>(qT, to(j, 0), to(j, 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    V8 bp, bs;
+    #pragma unroll
+                    for (int j = 0; j < TI; ++j) {
+                        const int qc = j / DB, db = j % DB;
+                        if (db == 0) {
+    #pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                bp[i] = (T)s[qc >> 1][8 * (qc & 1) + i];
+                                bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
+                            }
+                        }
+                        if constexpr (kAgpr) {
+                            mfma_agpr(dva[db], oa[j % kTf], bp);
+                            mfma_agpr(dka[db], ta[j % kTf], bs);
+                        } else {
+                            dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
+                            dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
+                        }
+                        if (j + kTf < TI) {
+                            oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
+                            ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
             // dS^T (bf16) to LDS: row = key within the block, columns = query rows
