@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
             // P and dS of 16-row chunk qc + 1 between the dV/dK products of chunk qc
             // (the two-pass form at d = 64: one wave per SIMD, so no other wave fills
             // the matrix core while this one does vector work; measured 4% faster).
-            // At d = 128 it measured no faster, and the padded d = 32 kernel would
+            // At d = 128 it measured 7% slower, and the padded d = 32 kernel would
             // lose a wave per SIMD, so every other kernel keeps the order below.
             constexpr bool kChunked = !DQ && D == 64 && DH == 64;
             if constexpr (kChunked) {
