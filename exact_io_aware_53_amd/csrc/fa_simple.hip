@@ -75,11 +75,35 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Rows [r0, r0 + kTile) of a [N, D] fp32 head, 16 bytes per load, into
+// registers (zeros past N); each thread holds kTile * D / (4 kThreads) of them.
+template <int D>
+struct TileRegs {
+    static constexpr int NV = kTile * D / (4 * kThreads);
+    static_assert(NV * 4 * kThreads == kTile * D, "a tile is whole 16-byte groups per thread");
+    float4 x[NV];
+    __device__ __forceinline__ void load(const float* src, int r0, int N) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = (i * kThreads + threadIdx.x) * 4, r = e / D, c = e % D;
+            x[i] = r0 + r < N ? *(const float4*)(src + (size_t)(r0 + r) * D + c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+    __device__ __forceinline__ void store(float (*dst)[D]) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = (i * kThreads + threadIdx.x) * 4, r = e / D, c = e % D;
+            *(float4*)&dst[r][c] = x[i];
+        }
+    }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
+    static_assert(sizeof(T) == 4, "the forward stages fp32 rows");
     constexpr int DC = D / kFLanes;
-    __shared__ float ks[kTile][D];
-    __shared__ float vs[kTile][D];
+    __shared__ __attribute__((aligned(16))) float ks[kTile][D];
+    __shared__ __attribute__((aligned(16))) float vs[kTile][D];
     const int nblk = (p.N + kFRows - 1) / kFRows;
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int b = bh / p.H, h = bh % p.H;
@@ -97,11 +121,20 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(SimpleParams p) {
     float m = -INFINITY, l = 0.0f;
     const int last_row = min(p.N, (blk + 1) * kFRows) - 1;
     const int key_end = p.causal ? last_row + 1 : p.N;
+    // K/V tiles double-buffered through registers: the loads of tile t + 1 are in
+    // flight while tile t is computed from LDS.
+    TileRegs<D> kr, vr;
+    kr.load((const float*)k, 0, p.N);
+    vr.load((const float*)v, 0, p.N);
     for (int k0 = 0; k0 < key_end; k0 += kTile) {
         __syncthreads();
-        stage_rows<T, D>(ks, k, k0, p.N);
-        stage_rows<T, D>(vs, v, k0, p.N);
+        kr.store(ks);
+        vr.store(vs);
         __syncthreads();
+        if (k0 + kTile < key_end) {
+            kr.load((const float*)k, k0 + kTile, p.N);
+            vr.load((const float*)v, k0 + kTile, p.N);
+        }
         float s[kTile];
 #pragma unroll
         for (int j = 0; j < kTile; ++j) {
