@@ -117,7 +117,7 @@ __device__ __forceinline__ void decode_block(int bid, int heads, int nqb, bool r
 }
 
 template <typename T, int D, int BC, int NW, int RB, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && D == 64 && BC == 64 ? 4 : RB == 1 && D <= 128 ? 2 : 1)))
 void fwd_kernel(FwdParams p) {
     using V8 = typename Vec<T>::x8;
     using V4 = typename Vec<T>::x4;
@@ -404,9 +404,15 @@ void fwd_kernel(FwdParams p) {
 // d = 256 takes 64-key tiles (two 128-key K/V tiles would not fit in LDS) and
 // 4 waves with up to 512 registers each: the Q rows (64 registers) and the
 // output accumulator (128) leave too little of 256 for the score tile.
+// At d = 64 without dropout a second kernel takes 64-key tiles: 43 KB of LDS
+// and at most 128 registers per lane let two workgroups (four waves per SIMD)
+// share a CU, which pays once the grid gives every CU two workgroups (measured:
+// +11% non-causal at B4 H16 N2048, +4.5% causal at B1 H16 N16384) and costs
+// 2-4% on a grid of one workgroup per CU, where the 128-key kernel stays.
 #ifndef FA_FWD_BC
 #define FA_FWD_BC 128
 #endif
+constexpr int kFwdTwoPerCu = 2 * 256;   // workgroups that fill MI355X's 256 CUs twice
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 8
 #endif
@@ -415,10 +421,22 @@ void fwd_kernel(FwdParams p) {
 #define FA_FWD_RB 1
 #endif
 
-template <typename T, int D, bool CAUSAL, bool DROPOUT>
+template <int D>
+constexpr int fwd_rows() { return (D == 256 ? 4 : FA_FWD_NW) * 32 * FA_FWD_RB; }
+
+// Workgroups of the forward grid: one per pair of query blocks of a head when
+// causal (a short and a long one), one per query block otherwise.
+template <int D>
+long long fwd_workgroups(const FwdArgs& a) {
+    const long long nqb = (a.s.N + fwd_rows<D>() - 1) / fwd_rows<D>();
+    return (long long)a.s.B * a.s.H * (a.s.causal ? (nqb + 1) / 2 : nqb);
+}
+
+template <typename T, int D, int BC, bool CAUSAL, bool DROPOUT>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-    constexpr int BC = D == 256 ? 64 : FA_FWD_BC, NW = D == 256 ? 4 : FA_FWD_NW, RB = FA_FWD_RB;
+    constexpr int NW = D == 256 ? 4 : FA_FWD_NW, RB = FA_FWD_RB;
     constexpr int BR = NW * 32 * RB;
+    static_assert(BR == fwd_rows<D>(), "grid rows");
     FwdParams p{};
     p.q = a.q;
     p.k = a.k;
@@ -446,11 +464,19 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
+hipError_t launch_tiles(const FwdArgs& a, hipStream_t st) {
+    if constexpr (D == 64 && !DROPOUT) {
+        if (fwd_workgroups<D>(a) >= kFwdTwoPerCu) return launch_cfg<T, D, 64, CAUSAL, false>(a, st);
+    }
+    return launch_cfg<T, D, D == 256 ? 64 : FA_FWD_BC, CAUSAL, DROPOUT>(a, st);
+}
+
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     const bool drop = dropout_threshold(a.s.dropout_p) != 0;
-    if (a.s.causal) return drop ? launch_cfg<T, D, true, true>(a, st) : launch_cfg<T, D, true, false>(a, st);
-    return drop ? launch_cfg<T, D, false, true>(a, st) : launch_cfg<T, D, false, false>(a, st);
+    if (a.s.causal) return drop ? launch_tiles<T, D, true, true>(a, st) : launch_tiles<T, D, true, false>(a, st);
+    return drop ? launch_tiles<T, D, false, true>(a, st) : launch_tiles<T, D, false, false>(a, st);
 }
 
 

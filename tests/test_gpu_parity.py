@@ -314,6 +314,26 @@ def test_forward_wide_score_range(d, causal, p):
                         tag=f"d={d} causal={causal} p={p}")
 
 
+# d = 64 grids of at least 512 workgroups (two per CU) run the forward with
+# 64-key tiles and two workgroups per CU; smaller grids keep 128-key tiles.
+# B*H = 64 heads; 256 query rows per workgroup, causal grids pair two blocks.
+TWO_PER_CU = [(1, 64, 2048, 64, False, 1.0), (1, 64, 1999, 64, False, 16.0),
+              (1, 64, 4096, 64, True, 1.0), (1, 64, 3969, 64, True, 16.0)]
+
+
+@pytest.mark.parametrize("case", TWO_PER_CU, ids=lambda c: "x".join(map(str, c[:4])) + f"-causal{int(c[4])}-q{c[5]:g}")
+def test_forward_d64_two_workgroups_per_cu(case):
+    """The 64-key-tile forward against the oracle, on sampled heads spread over
+    the XCD groups, with a ragged tail and (Q x 16) the rescale path."""
+    B, H, N, d, causal, qmul = case
+    q, k, v = normal_tensors((B, H, N, d), 4100 + N, 3, torch.bfloat16)
+    q = (q.float() * qmul).to(torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=0.0, seed=SEED)
+    torch.cuda.synchronize()
+    check_forward_heads(q, k, v, o, lse, causal, 0.0, SEED, TOL["bf16"], [(0, 0), (0, 9), (0, 38), (0, 63)],
+                        tag=str(case))
+
+
 def test_forward_takes_no_device_memory_and_inputs_grow_linearly():
     """The forward needs no workspace: with outputs preallocated, free device
     memory is the same before and after a call at every N; the tensors a call
