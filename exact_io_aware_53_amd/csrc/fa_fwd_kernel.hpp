@@ -412,7 +412,8 @@ void fwd_kernel(FwdParams p) {
 #ifndef FA_FWD_BC
 #define FA_FWD_BC 128
 #endif
-constexpr int kFwdTwoPerCu = 2 * 256;   // workgroups that fill MI355X's 256 CUs twice
+constexpr int kFwdOnePerCu = 256;                // MI355X's compute units
+constexpr int kFwdTwoPerCu = 2 * kFwdOnePerCu;   // workgroups that fill them twice
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 8
 #endif
@@ -421,22 +422,20 @@ constexpr int kFwdTwoPerCu = 2 * 256;   // workgroups that fill MI355X's 256 CUs
 #define FA_FWD_RB 1
 #endif
 
-template <int D>
-constexpr int fwd_rows() { return (D == 256 ? 4 : FA_FWD_NW) * 32 * FA_FWD_RB; }
-
-// Workgroups of the forward grid: one per pair of query blocks of a head when
-// causal (a short and a long one), one per query block otherwise.
-template <int D>
+// Workgroups of the forward grid with NW waves (32 * RB query rows each) per
+// workgroup: one per pair of query blocks of a head when causal (a short and a
+// long one), one per query block otherwise.
+template <int NW>
 long long fwd_workgroups(const FwdArgs& a) {
-    const long long nqb = (a.s.N + fwd_rows<D>() - 1) / fwd_rows<D>();
+    constexpr int BR = NW * 32 * FA_FWD_RB;
+    const long long nqb = (a.s.N + BR - 1) / BR;
     return (long long)a.s.B * a.s.H * (a.s.causal ? (nqb + 1) / 2 : nqb);
 }
 
-template <typename T, int D, int BC, bool CAUSAL, bool DROPOUT>
+template <typename T, int D, int BC, int NW, bool CAUSAL, bool DROPOUT>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-    constexpr int NW = D == 256 ? 4 : FA_FWD_NW, RB = FA_FWD_RB;
+    constexpr int RB = FA_FWD_RB;
     constexpr int BR = NW * 32 * RB;
-    static_assert(BR == fwd_rows<D>(), "grid rows");
     FwdParams p{};
     p.q = a.q;
     p.k = a.k;
@@ -466,10 +465,22 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
 hipError_t launch_tiles(const FwdArgs& a, hipStream_t st) {
-    if constexpr (D == 64 && !DROPOUT) {
-        if (fwd_workgroups<D>(a) >= kFwdTwoPerCu) return launch_cfg<T, D, 64, CAUSAL, false>(a, st);
+    if constexpr (D == 256) {
+        return launch_cfg<T, D, 64, 4, CAUSAL, DROPOUT>(a, st);
+    } else {
+        constexpr int NW = FA_FWD_NW;
+        if constexpr (D == 64 && !DROPOUT) {
+            if (fwd_workgroups<NW>(a) >= kFwdTwoPerCu) return launch_cfg<T, D, 64, NW, CAUSAL, false>(a, st);
+        }
+        if constexpr (NW == 8) {
+            // A grid that leaves CUs idle: halving the rows per workgroup doubles
+            // the workgroups. As long as they still fit one round (one per CU),
+            // the chip finishes in about half the time, though a wave per SIMD
+            // hides less latency than two.
+            if (fwd_workgroups<4>(a) <= kFwdOnePerCu) return launch_cfg<T, D, FA_FWD_BC, 4, CAUSAL, DROPOUT>(a, st);
+        }
+        return launch_cfg<T, D, FA_FWD_BC, NW, CAUSAL, DROPOUT>(a, st);
     }
-    return launch_cfg<T, D, D == 256 ? 64 : FA_FWD_BC, CAUSAL, DROPOUT>(a, st);
 }
 
 template <typename T, int D>

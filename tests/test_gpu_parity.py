@@ -334,6 +334,35 @@ def test_forward_d64_two_workgroups_per_cu(case):
                         tag=str(case))
 
 
+# A grid that fits 256 workgroups of 128 query rows (one per CU) runs the
+# forward with 4-wave workgroups: the small shapes above all take that path.
+# These shapes give more workgroups than that, so they run the 8-wave kernel
+# (256 rows per workgroup) on ragged tails, with and without dropout.
+EIGHT_WAVE = [(1, 160, 300, 128), (2, 80, 257, 64), (1, 160, 300, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.1])
+@pytest.mark.parametrize("shape", EIGHT_WAVE, ids=lambda s: "x".join(map(str, s)))
+def test_forward_eight_wave_grids(shape, causal, p):
+    B, H, N, d = shape
+    q, k, v = normal_tensors(shape, 5200 + N + d, 3, torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=p, seed=SEED)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 1), (0, 37), (B - 1, H - 2), (B - 1, H - 1)]
+    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL["bf16"], heads, tag=str(shape))
+
+
+def test_forward_four_wave_grid_at_the_limit():
+    """B1 H16 N4096 d128 causal: 16 heads x 16 pairs of 128-row blocks = 256
+    workgroups, the largest grid that takes the 4-wave kernel."""
+    B, H, N, d = 1, 16, 4096, 128
+    q, k, v = normal_tensors((B, H, N, d), 5301, 3, torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=True, dropout_p=0.0, seed=SEED)
+    torch.cuda.synchronize()
+    check_forward_heads(q, k, v, o, lse, True, 0.0, SEED, TOL["bf16"], [(0, 0), (0, 15)], tag="b1h16n4096d128")
+
+
 def test_forward_takes_no_device_memory_and_inputs_grow_linearly():
     """The forward needs no workspace: with outputs preallocated, free device
     memory is the same before and after a call at every N; the tensors a call
