@@ -476,8 +476,12 @@ hipError_t launch_tiles(const FwdArgs& a, hipStream_t st) {
             // A grid that leaves CUs idle: halving the rows per workgroup doubles
             // the workgroups. As long as they still fit one round (one per CU),
             // the chip finishes in about half the time, though a wave per SIMD
-            // hides less latency than two.
-            if (fwd_workgroups<4>(a) <= kFwdOnePerCu) return launch_cfg<T, D, FA_FWD_BC, 4, CAUSAL, DROPOUT>(a, st);
+            // hides less latency than two. Where halving adds no workgroups (a
+            // causal head of 129-256 rows: one pair of short blocks instead of
+            // one block) it only lengthens each workgroup's walk.
+            const long long w4 = fwd_workgroups<4>(a);
+            if (w4 <= kFwdOnePerCu && w4 > fwd_workgroups<NW>(a))
+                return launch_cfg<T, D, FA_FWD_BC, 4, CAUSAL, DROPOUT>(a, st);
         }
         return launch_cfg<T, D, FA_FWD_BC, NW, CAUSAL, DROPOUT>(a, st);
     }
