@@ -276,9 +276,16 @@ int fa_fwd_ex(const fa_problem* pb, const void* q, const void* k, const void* v,
 // Width the backward computes at: head sizes 32 and 96 run on rows padded to 64 and 128.
 int compute_width(int d) { return d == 32 ? 64 : d == 96 ? 128 : d; }
 
+// One head's fp32 dQ accumulator rows (ragged tail tiles included) must stay
+// within the 32-bit byte range of the buffer resource that addresses them, as
+// check_shape requires of fa_bwd: past it the range would wrap and the dQ
+// atomics would be dropped.
+bool dq_acc_head_ok(int N, int dc) { return (long long)(N + 256) * dc * 4 < kHeadBytes; }
+
 size_t fa_bwd_ex_workspace_size(const fa_problem* pb) {
     fa::TensorLayouts L;
     if (problem_layouts(pb, true, L) != FA_OK) return 0;
+    if (!dq_acc_head_ok(pb->N, compute_width(pb->d))) return 0;
     return workspace_bytes(pb->B, pb->H, pb->N, compute_width(pb->d));
 }
 
@@ -299,6 +306,7 @@ int fa_bwd_ex(const fa_problem* pb, const void* q, const void* k, const void* v,
     if (!(dropout_p >= 0.0f && dropout_p < 1.0f)) return FA_ERR_INVALID_ARG;
     const int B = pb->B, H = pb->H, N = pb->N, dc = compute_width(pb->d);
     if ((long long)B * H * N * dc > kMaxElems) return FA_ERR_INVALID_ARG;   // workspace indexing
+    if (!dq_acc_head_ok(N, dc)) return FA_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(B, H, N, dc)) return FA_ERR_INVALID_ARG;
     const size_t rows = (size_t)B * H * N;
     float* dq_acc = (float*)workspace;

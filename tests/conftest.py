@@ -8,3 +8,15 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Raw O / LSE errors of every parity check of the run."""
+    try:
+        from parity_checks import REPORT
+    except ImportError:
+        return
+    if REPORT:
+        terminalreporter.section("parity: raw errors against the oracle")
+        for line in REPORT:
+            terminalreporter.write_line(line)

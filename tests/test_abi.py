@@ -225,4 +225,9 @@ def test_bwd_ex_workspace(L):
     assert bwd_ex(L, pb, ws=None) == inv
     assert bwd_ex(L, pb, ws=FAKE * 16 + 8) == inv
     assert bwd_ex(L, problem(dq=fa.Layout(0, 0, 8))) == inv                   # dq rows overlap
+    # one head's fp32 dQ accumulator past 32-bit byte offsets (its bf16 rows are not)
+    big = problem(B=1, H=1, N=2**23, d=128)
+    assert L.fa_bwd_ex_workspace_size(ctypes.byref(big)) == 0
+    assert bwd_ex(L, big, ws_bytes=1 << 40) == inv
+    assert L.fa_bwd_ex_workspace_size(ctypes.byref(problem(B=1, H=1, N=2**22, d=128))) > 0
     assert L.fa_bwd_ex_workspace_size(None) == 0

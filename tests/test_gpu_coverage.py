@@ -4,8 +4,8 @@ fp64 oracle: head sizes 32, 96 and 256, fp16 next to bf16, strided layouts
 variable-length batches.
 
 Bars (the bf16 ones, which fp16's 11-bit significand meets a fortiori):
-O max|err| <= 1e-2 (widened only where half a storage ulp of O alone exceeds
-it), LSE <= 1e-3, gradients max|g - g_ref| / max|g_ref| <= 2e-2. A strided
+O max|err| <= 1e-2 (plus half a storage ulp only where |O_ref| >= 4, see
+parity_checks), LSE <= 1e-3, gradients max|g - g_ref| / max|g_ref| <= 2e-2. A strided
 call must give exactly the bits of the same call on contiguous copies: the
 kernels do the same arithmetic, only the addresses differ.
 """
@@ -18,12 +18,13 @@ import torch
 import exact_io_aware_53_amd as fa
 import oracle
 from exact_io_aware_53_amd.inputs import normal_tensors, to_f64
+from parity_checks import Stats
 
 pytestmark = pytest.mark.gpu
 
 SEED = 0x5EED0F00D
 DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
-O_TOL, LSE_TOL, GRAD_TOL = 1e-2, 1e-3, 2e-2
+GRAD_TOL = 2e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,18 +32,6 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     fa.lib()
-
-
-def half_ulp(x, dtype):
-    bits = 8 if dtype == torch.bfloat16 else 11
-    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
-    return np.exp2(np.floor(np.log2(ax)) - bits)
-
-
-def o_excess(got, ref, dtype):
-    """max |got - ref| / bound, bound = 1e-2 widened where storage rounding alone exceeds it."""
-    bound = np.maximum(O_TOL, half_ulp(ref, dtype) + np.abs(ref) * 2.0 ** -9)
-    return float((np.abs(got - ref) / bound).max())
 
 
 def rel_to_max(g, ref, fallback):
@@ -54,15 +43,14 @@ def rel_to_max(g, ref, fallback):
     return float(np.abs(g - ref).max() / denom)
 
 
-def check_head(q, k, v, o, lse, causal, p, b, h, dtype, do=None, grads=None):
+def check_head(q, k, v, o, lse, causal, p, b, h, dtype, do=None, grads=None, tag=""):
     """q, k, v, do: [n, d] CPU tensors of one head (one sequence); o, lse, grads: GPU results."""
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d)
     ro, rl = oracle.forward(to_f64(q), to_f64(k), to_f64(v), scale, causal, p, SEED, b, h)
-    eo = o_excess(o.double().cpu().numpy(), ro, dtype)
-    el = float(np.abs(lse.double().cpu().numpy() - rl).max())
-    assert eo <= 1.0, f"O error {eo:.3f} of its bound (b={b}, h={h})"
-    assert el <= LSE_TOL, f"LSE error {el:.3e} (b={b}, h={h})"
+    st = Stats(dtype)
+    st.add(o.double().cpu().numpy(), ro, lse.double().cpu().numpy(), rl)
+    st.check(f"{tag} b={b} h={h}")
     if grads is None:
         return
     rq, rk, rv, _ = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal, p,
@@ -94,7 +82,8 @@ def test_fwd_bwd_head_sizes_and_dtypes(shape, causal, p, dtype):
     for b in range(B):
         for h in range(H):
             check_head(q[b, h], k[b, h], v[b, h], o[b, h], lse[b, h], causal, p, b, h, dt,
-                       do[b, h], (dq[b, h], dk[b, h], dv[b, h]))
+                       do[b, h], (dq[b, h], dk[b, h], dv[b, h]),
+                       tag=f"fwd_ex {shape} {dtype} causal={causal} p={p}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -139,7 +128,7 @@ def test_bshd_layout_equals_contiguous(d, dtype):
         assert torch.equal(a, b)
     torch.cuda.synchronize()
     check_head(q[1, 2], k[1, 2], v[1, 2], o_s[1, 2], l_s[1, 2], True, 0.1, 1, 2, dt, do[1, 2],
-               (g_s[0][1, 2], g_s[1][1, 2], g_s[2][1, 2]))
+               (g_s[0][1, 2], g_s[1][1, 2], g_s[2][1, 2]), tag=f"[B,N,H,d] d={d} {dtype}")
 
 
 def test_packed_qkv_views():
@@ -153,7 +142,8 @@ def test_packed_qkv_views():
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
     torch.cuda.synchronize()
     qc, kc, vc = (t.cpu() for t in (q, k, v))
-    check_head(qc[1, 3], kc[1, 3], vc[1, 3], o[1, 3], lse[1, 3], True, 0.0, 1, 3, torch.bfloat16)
+    check_head(qc[1, 3], kc[1, 3], vc[1, 3], o[1, 3], lse[1, 3], True, 0.0, 1, 3, torch.bfloat16,
+               tag="packed QKV views")
 
 
 # ------------------------------------------------------------ packed batches
@@ -189,7 +179,8 @@ def test_varlen_forward_backward(d, causal):
         s = slice(int(cu[b]), int(cu[b + 1]))
         for h in range(H):
             check_head(q[s, h], k[s, h], v[s, h], o[s, h], lse[h, s], causal, p, b, h, dt,
-                       do[s, h], (dq[s, h], dk[s, h], dv[s, h]))
+                       do[s, h], (dq[s, h], dk[s, h], dv[s, h]),
+                       tag=f"varlen d={d} causal={causal} len={n}")
 
 
 def test_varlen_equals_padded_batch():
@@ -215,7 +206,8 @@ def test_varlen_clamps_oversized_offsets():
     o, lse = fa.fwd_varlen(gq, gk, gv, torch.from_numpy(cu_np).cuda(), 256, causal=True)
     torch.cuda.synchronize()
     s = slice(100, 160)
-    check_head(q[s, 0], k[s, 0], v[s, 0], o[s, 0], lse[0, s], True, 0.0, 1, 0, torch.bfloat16)
+    check_head(q[s, 0], k[s, 0], v[s, 0], o[s, 0], lse[0, s], True, 0.0, 1, 0, torch.bfloat16,
+               tag="varlen clamped offsets")
 
 
 # ------------------------------------------------------ full-size workloads
@@ -257,4 +249,4 @@ def test_coverage_workload_sampled_head(name):
         res = (o[b, h], lse[b, h])
         gr = tuple(x[b, h] for x in grads)
         dout = view(t["do"])[b, h]
-    check_head(*args, *res, w.causal, 0.0, b, h, w.torch_dtype, dout, gr)
+    check_head(*args, *res, w.causal, 0.0, b, h, w.torch_dtype, dout, gr, tag=f"coverage workload {name}")

@@ -15,7 +15,7 @@ import torch
 import exact_io_aware_53_amd as fa
 import oracle
 from exact_io_aware_53_amd.inputs import DECODE_WORKLOADS, make_decode_inputs, sample_heads, to_f64
-from test_gpu_parity import TOL, o_bound
+from parity_checks import Stats
 
 pytestmark = pytest.mark.gpu
 
@@ -37,15 +37,12 @@ def check_decode(q, k, v, o, lse, causal, heads, tag=""):
     Nq, Nk, d = q.shape[2], k.shape[2], q.shape[3]
     scale = 1.0 / math.sqrt(d)
     o_c, l_c = o.float().cpu(), lse.cpu()
-    worst_o = worst_l = 0.0
+    st = Stats(torch.bfloat16)
     for (b, h) in heads:
         ro, rl = oracle.forward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale, causal,
                                 key_offset=Nk - Nq)
-        go, gl = o_c[b, h].double().numpy(), l_c[b, h].double().numpy()
-        eo = (np.abs(go - ro) / o_bound(ro, TOL["bf16"]["o"], torch.bfloat16)).max() * TOL["bf16"]["o"]
-        worst_o, worst_l = max(worst_o, eo), max(worst_l, np.abs(gl - rl).max())
-    assert worst_o <= TOL["bf16"]["o"], f"{tag} O err {worst_o:.3e}"
-    assert worst_l <= TOL["bf16"]["lse"], f"{tag} LSE err {worst_l:.3e}"
+        st.add(o_c[b, h].double().numpy(), ro, l_c[b, h].double().numpy(), rl)
+    st.check(f"decode {tag}")
 
 
 # (B, H, Nq, Nk, d): one key; one chunk (Nk <= 128); many chunks with a ragged
@@ -154,9 +151,9 @@ def check_paged(q, k, v, lens, o, lse, causal, tag):
                 continue
             ro, rl = oracle.forward(to_f64(q[b, h]), to_f64(k[b, h, :n]), to_f64(v[b, h, :n]), scale,
                                     causal, rows=np.array(rows), key_offset=off)
-            eo = (np.abs(go[rows] - ro) / o_bound(ro, TOL["bf16"]["o"], torch.bfloat16)).max() * TOL["bf16"]["o"]
-            el = np.abs(gl[rows] - rl).max()
-            assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"], f"{tag} b{b} h{h}: O {eo:.2e} LSE {el:.2e}"
+            st = Stats(torch.bfloat16)
+            st.add(go[rows], ro, gl[rows], rl)
+            st.check(f"paged decode {tag} b{b} h{h}")
 
 
 PAGED_CASES = [  # (H, Nq, lens, page, d)

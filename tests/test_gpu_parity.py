@@ -1,21 +1,16 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
 
-Tolerances: fp32 tensors max |err| <= 1e-5 (O, LSE and gradients); bf16
-tensors O <= 1e-2, LSE <= 1e-3, gradients max|g - g_ref| / max|g_ref| <= 2e-2;
+Bars: fp32 tensors max |err| <= 1e-5 (O, LSE and gradients); bf16 tensors
+O <= 1e-2 (plus half a storage ulp only where |O_ref| >= 4, see
+parity_checks), LSE <= 1e-3, gradients max|g - g_ref| / max|g_ref| <= 2e-2;
 dropout masks bit-exact. Small shapes are checked on every row of every
 head; the full-size workloads on seeded heads and rows (full rows always).
 
-Two readings of those bounds, both forced by the output dtype:
-* O is stored in bf16. Where |O_ref| >= 4 (rows that mix only a few keys,
-  e.g. causal row 0 scaled by 1/(1-p)), half a bf16 ulp alone exceeds 1e-2,
-  so no bf16 result could meet it. There the bound per element is
-  half an ulp of O_ref plus 2^-9 |O_ref| (the rounding of P to bf16); below
-  |O_ref| = 4 that expression is under 1e-2 and the plain bound applies.
-* A gradient whose reference is zero by the mathematics (one visible key, or
-  a dropped single key) has no "max": fp64 leaves it as rounding noise of
-  order 1e-17. Such a reference (max below 1e-9 of the head's largest
-  reference gradient) is measured relative to that largest gradient, or
-  absolutely if all three are zero.
+A gradient whose reference is zero by the mathematics (one visible key, or a
+dropped single key) has no "max": fp64 leaves it as rounding noise of order
+1e-17. Such a reference (max below 1e-9 of the head's largest reference
+gradient) is measured relative to that largest gradient, or absolutely if
+all three are zero.
 """
 import math
 
@@ -27,6 +22,7 @@ import exact_io_aware_53_amd as fa
 import oracle
 from exact_io_aware_53_amd.inputs import (WORKLOADS, make_inputs, normal_tensors, sample_heads,
                                           sample_rows, to_f64)
+from parity_checks import Stats, p_rounding_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -46,38 +42,27 @@ def upload(ts):
     return [t.to("cuda") for t in ts]
 
 
-def check_forward_heads(q, k, v, o, lse, causal, p, seed, tol, heads, rows=None, tag=""):
-    """Compare O and LSE of the given heads (all rows, or `rows`) with the oracle."""
+def check_forward_heads(q, k, v, o, lse, causal, p, seed, tol, heads, rows=None, tag="",
+                        wide_scores=False):
+    """Compare O and LSE of the given heads (all rows, or `rows`) with the oracle.
+    wide_scores: the Q x16 stress inputs, where an element that misses the bar must
+    lie within the bf16 P~ rounding bound (parity_checks)."""
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d)
     o_c, lse_c = o.float().cpu(), lse.cpu()
-    worst_o = worst_l = 0.0
+    st = Stats(o.dtype)
     for (b, h) in heads:
-        ro, rl = oracle.forward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), scale,
-                                causal, p, seed, b, h, rows=rows)
+        qh, kh, vh = to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h])
+        ro, rl = oracle.forward(qh, kh, vh, scale, causal, p, seed, b, h, rows=rows)
         go = o_c[b, h].double().numpy()
         gl = lse_c[b, h].double().numpy()
         if rows is not None:
             go, gl = go[rows], gl[rows]
-        excess = np.abs(go - ro) / o_bound(ro, tol["o"], o.dtype)
-        eo, el = excess.max() * tol["o"], np.abs(gl - rl).max()
-        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
-    assert worst_o <= tol["o"], f"{tag} O max err (scaled to the 1e-2 bound) {worst_o:.3e}"
-    assert worst_l <= tol["lse"], f"{tag} LSE max err {worst_l:.3e}"
-    return worst_o, worst_l
-
-
-def bf16_half_ulp(x):
-    """Half the spacing of bf16 numbers at |x| (8 significand bits)."""
-    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
-    return np.exp2(np.floor(np.log2(ax)) - 8)
-
-
-def o_bound(ref, tol, dtype):
-    """Per-element O bound: tol, widened only where bf16 storage alone exceeds it."""
-    if dtype != torch.bfloat16:
-        return np.full(ref.shape, tol)
-    return np.maximum(tol, bf16_half_ulp(ref) + np.abs(ref) * 2.0 ** -9)
+        pr = (p_rounding_bound(qh, kh, vh, ro, rl, scale, causal, p, seed, b, h, rows)
+              if wide_scores else None)
+        st.add(go, ro, gl, rl, p_round=pr)
+    st.check(tag or f"{tuple(q.shape)} causal={causal} p={p}")
+    return st.err_o, st.err_lse
 
 
 def rel_to_max(g, ref, fallback=None):
@@ -116,7 +101,8 @@ def test_forward_small(shape, causal, p, dtype):
     o, lse = fa.fwd(gq, gk, gv, causal=causal, dropout_p=p, seed=SEED)
     torch.cuda.synchronize()
     heads = [(b, h) for b in range(B) for h in range(H)]
-    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL[dtype], heads, tag=str(shape))
+    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL[dtype], heads,
+                        tag=f"forward {shape} {dtype} causal={causal} p={p}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -157,14 +143,15 @@ def run_workload_forward(w):
 def test_workload_f32_b1h1n128d64():
     w = WORKLOADS["fwd_f32_b1h1n128d64"]
     t, _, o, lse = run_workload_forward(w)
-    check_forward_heads(t["q"], t["k"], t["v"], o, lse, w.causal, 0.0, 0, TOL["f32"], [(0, 0)])
+    check_forward_heads(t["q"], t["k"], t["v"], o, lse, w.causal, 0.0, 0, TOL["f32"], [(0, 0)],
+                        tag="fwd_f32_b1h1n128d64 (all rows)")
 
 
 def test_workload_causal_b4h16n2048d64():
     w = WORKLOADS["fwd_causal_bf16_b4h16n2048d64"]
     t, _, o, lse = run_workload_forward(w)
     check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
-                        sample_heads(w, 2))
+                        sample_heads(w, 2), tag="fwd_causal_bf16_b4h16n2048d64 (2 heads, all rows)")
 
 
 def test_workload_causal_q4_b2h32n8192d128():
@@ -172,7 +159,8 @@ def test_workload_causal_q4_b2h32n8192d128():
     t, _, o, lse = run_workload_forward(w)
     rows = sample_rows(w, 256, block_rows=(64, 128, 256))
     check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
-                        sample_heads(w, 2), rows=rows)
+                        sample_heads(w, 2), rows=rows,
+                        tag=f"fwd_causal_q4_bf16_b2h32n8192d128 (2 heads x {len(rows)} rows)")
 
 
 def test_workload_causal_b1h16n32768d128():
@@ -180,7 +168,8 @@ def test_workload_causal_b1h16n32768d128():
     t, _, o, lse = run_workload_forward(w)
     rows = sample_rows(w, 64, block_rows=(64, 128, 256))
     check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, 0.0, 0, TOL["bf16"],
-                        sample_heads(w, 2), rows=rows)
+                        sample_heads(w, 2), rows=rows,
+                        tag=f"fwd_causal_bf16_b1h16n32768d128 (2 heads x {len(rows)} rows)")
 
 
 def test_workload_dropout_fwd_bwd_b2h16n4096d64():
@@ -193,7 +182,7 @@ def test_workload_dropout_fwd_bwd_b2h16n4096d64():
     torch.cuda.synchronize()
     (b, h), = sample_heads(w, 1)
     check_forward_heads(t["q"], t["k"], t["v"], o, lse, True, w.dropout_p, w.dropout_seed,
-                        TOL["bf16"], [(b, h)])
+                        TOL["bf16"], [(b, h)], tag="fwdbwd_causal_dropout_bf16_b2h16n4096d64 (1 head)")
     rq, rk, rv, _ = oracle.backward(to_f64(t["q"][b, h]), to_f64(t["k"][b, h]),
                                     to_f64(t["v"][b, h]), to_f64(t["do"][b, h]), w.scale, True,
                                     w.dropout_p, w.dropout_seed, b, h)
@@ -244,6 +233,85 @@ def test_dropout_mask_through_backward_kernel():
         got = (dv.float().cpu().numpy()[0, 0] != 0).T        # [c, j]
         ref = oracle.keep_mask(0, 0, rows, np.arange(N), p, SEED)
         assert np.array_equal(got, ref), i0
+
+
+# Probes on the kernel instances of the dropout workload itself (B2 H16 N4096
+# d64, causal, p = 0.1): its grid takes the 8-wave causal dropout forward, the
+# causal key-side backward with fused dQ atomics and, in the two-pass form, the
+# chunked d = 64 key side and the query-side dQ pass. Each probe reads the mask
+# out of a product whose element is a nonzero multiple of Z_ij, so any wrong
+# counter shows as a mismatch with the oracle's mask; causal entries j > i must
+# come out zero.
+C4 = "fwdbwd_causal_dropout_bf16_b2h16n4096d64"
+PROBE_HEADS = [(0, 0), (1, 15)]
+PROBE_WINDOWS = (0, 1990, 4032)
+
+
+def causal_keep(b, h, rows, cols, w):
+    keep = oracle.keep_mask(b, h, rows, cols, w.dropout_p, w.dropout_seed)
+    return keep & (np.asarray(cols)[None, :] <= np.asarray(rows)[:, None])
+
+
+def test_dropout_mask_through_causal_forward_workload_kernel():
+    """V = one-hot columns (V[j_c, c] = 1): O[i, c] = P_{i j_c} Z_{i j_c} / (1-p)."""
+    w = WORKLOADS[C4]
+    t = make_inputs(w)
+    gq, gk = upload((t["q"], t["k"]))
+    rows = np.arange(w.N)
+    for j0 in PROBE_WINDOWS:
+        cols = np.arange(j0, j0 + w.d)
+        v = torch.zeros((w.B, w.H, w.N, w.d), dtype=torch.bfloat16)
+        v[:, :, torch.as_tensor(cols), torch.arange(w.d)] = 1.0
+        o, _ = fa.fwd(gq, gk, v.cuda(), causal=True, dropout_p=w.dropout_p, seed=w.dropout_seed)
+        got = o.float().cpu().numpy() != 0
+        for (b, h) in PROBE_HEADS:
+            assert np.array_equal(got[b, h], causal_keep(b, h, rows, cols, w)), (j0, b, h)
+
+
+@pytest.mark.parametrize("deterministic", [False, True], ids=["fused", "two_pass"])
+def test_dropout_mask_through_causal_backward_dv(deterministic):
+    """dO rows i_c = e_c: dV_j[c] = P_{i_c j} Z_{i_c j} / (1-p), 64 mask rows per launch,
+    through the key-side kernel (fused dQ atomics, or the two-pass key side)."""
+    w = WORKLOADS[C4]
+    t = make_inputs(w)
+    gq, gk, gv = upload((t["q"], t["k"], t["v"]))
+    _, lse = fa.fwd(gq, gk, gv, causal=True)
+    o = torch.zeros_like(gq)
+    cols = np.arange(w.N)
+    for i0 in PROBE_WINDOWS:
+        rows = np.arange(i0, i0 + w.d)
+        do = torch.zeros((w.B, w.H, w.N, w.d), dtype=torch.bfloat16)
+        do[:, :, torch.as_tensor(rows), torch.arange(w.d)] = 1.0
+        _, _, dv = fa.bwd(gq, gk, gv, o, lse, do.cuda(), causal=True, dropout_p=w.dropout_p,
+                          seed=w.dropout_seed, deterministic=deterministic)
+        got = dv.float().cpu().numpy() != 0
+        for (b, h) in PROBE_HEADS:
+            assert np.array_equal(got[b, h].T, causal_keep(b, h, rows, cols, w)), (i0, b, h)
+
+
+@pytest.mark.parametrize("deterministic", [False, True], ids=["fused", "two_pass"])
+def test_dropout_mask_through_causal_backward_dq(deterministic):
+    """K and V one-hot on 64 keys j_c (K[j_c] = V[j_c] = e_c, every other row 0), dO all
+    ones, and O = 0 given to the backward, so D = 0 and dS_ij = P_ij Z_ij / (1-p) on the
+    probed keys and 0 elsewhere: dQ_i[c] = scale P_{i j_c} Z_{i j_c} / (1-p). That is the
+    fused kernel's dQ atomics, or the two-pass form's query-side pass."""
+    w = WORKLOADS[C4]
+    t = make_inputs(w)
+    gq = t["q"].cuda()
+    rows = np.arange(w.N)
+    do = torch.ones((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+    for j0 in PROBE_WINDOWS:
+        cols = np.arange(j0, j0 + w.d)
+        kv = torch.zeros((w.B, w.H, w.N, w.d), dtype=torch.bfloat16)
+        kv[:, :, torch.as_tensor(cols), torch.arange(w.d)] = 1.0
+        kv = kv.cuda()
+        _, lse = fa.fwd(gq, kv, kv, causal=True)
+        o = torch.zeros_like(gq)
+        dq, _, _ = fa.bwd(gq, kv, kv, o, lse, do, causal=True, dropout_p=w.dropout_p,
+                          seed=w.dropout_seed, deterministic=deterministic)
+        got = dq.float().cpu().numpy() != 0
+        for (b, h) in PROBE_HEADS:
+            assert np.array_equal(got[b, h], causal_keep(b, h, rows, cols, w)), (j0, b, h)
 
 
 # ------------------------------------------------------------ other properties
@@ -311,7 +379,7 @@ def test_forward_wide_score_range(d, causal, p):
     o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=p, seed=SEED)
     torch.cuda.synchronize()
     check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL["bf16"], [(0, 0), (0, 1)],
-                        tag=f"d={d} causal={causal} p={p}")
+                        tag=f"wide scores (Q x16) d={d} causal={causal} p={p}", wide_scores=True)
 
 
 # d = 64 grids of at least 512 workgroups (two per CU) run the forward with
@@ -331,7 +399,7 @@ def test_forward_d64_two_workgroups_per_cu(case):
     o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=0.0, seed=SEED)
     torch.cuda.synchronize()
     check_forward_heads(q, k, v, o, lse, causal, 0.0, SEED, TOL["bf16"], [(0, 0), (0, 9), (0, 38), (0, 63)],
-                        tag=str(case))
+                        tag=f"64-key forward {case}", wide_scores=qmul > 4.0)
 
 
 # A grid that fits 256 workgroups of 128 query rows (one per CU) runs the
@@ -350,7 +418,8 @@ def test_forward_eight_wave_grids(shape, causal, p):
     o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=p, seed=SEED)
     torch.cuda.synchronize()
     heads = [(0, 0), (0, 1), (0, 37), (B - 1, H - 2), (B - 1, H - 1)]
-    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL["bf16"], heads, tag=str(shape))
+    check_forward_heads(q, k, v, o, lse, causal, p, SEED, TOL["bf16"], heads,
+                        tag=f"8-wave forward {shape} causal={causal} p={p}")
 
 
 def test_forward_four_wave_grid_at_the_limit():
