@@ -37,6 +37,7 @@ SIGNATURES = {
     "fa_bwd_f32": (_I, _BWD_ARGS),
     "fa_bwd_deterministic": (_I, _BWD_ARGS),
     "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "fa_bwd_noalloc": (_I, _BWD_ARGS[:17] + [_P]),
     "fa_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "fa_fwd_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_fwd_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -296,6 +297,30 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout_p=0.0, seed=0,
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(q.device))
     _check(st, name)
+    return dq, dk, dv
+
+
+# Bytes of the library's own device scratch behind fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale=None, causal=False, dropout_p=0.0, seed=0):
+    """fa_bwd_noalloc: the bf16 backward with the library's own scratch, for
+    callers that cannot allocate. The output tensors are the caller's; nothing
+    is allocated here either."""
+    shp = _shape4(q, "q")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if _shape4(t, n) != shp or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, do, dq, dk, dv must share shape and dtype")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("fa_bwd_noalloc takes bfloat16 tensors")
+    B, H, N, d = shp
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                              scale, int(bool(causal)), float(dropout_p), int(seed) & (2**64 - 1),
+                              _stream(q.device))
+    _check(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

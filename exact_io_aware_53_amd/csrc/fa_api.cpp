@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "fa_launch.hpp"
 
 namespace fa {
@@ -120,19 +122,25 @@ int problem_layouts(const fa_problem* pb, bool backward, fa::TensorLayouts& L) {
     return FA_OK;
 }
 
+// Checks of the tensor arguments of fa_bwd and its variants (everything but the workspace).
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+              float scale, float dropout_p) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return check_shape(B, H, N, d, scale, dropout_p);
+}
+
 int bwd_common(bool bf16, const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv,
                int B, int H, int N, int d, float scale, int causal, float dropout_p,
                uint64_t seed, void* workspace, size_t ws_bytes, void* stream,
                bool deterministic = false) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-        return FA_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
-    const int st = check_shape(B, H, N, d, scale, dropout_p);
+    const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dropout_p);
     if (st != FA_OK) return st;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0) return FA_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_INVALID_ARG;
     const size_t rows = (size_t)B * H * N;
     float* dq_acc = (float*)workspace;
@@ -143,6 +151,33 @@ int bwd_common(bool bf16, const void* q, const void* k, const void* v, const voi
     a.L = fa::contiguous_layouts(H, N, d);
     hipStream_t s = (hipStream_t)stream;
     return map_hip(bf16 ? fa::launch_bwd_mfma(a, s) : fa::launch_bwd_f32(a, s));
+}
+
+// ---- device scratch of fa_bwd_noalloc ------------------------------------
+// The workspace of fa_bwd_noalloc lives in this array, one copy on every GPU the
+// library runs on, held until the process ends. In host code its name is only a
+// host-side stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_HIP;
+    if (dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::call_once(scratch_once[dev], [dev] {
+        void* p = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return FA_ERR_HIP;
+    *out = scratch_ptr[dev];
+    return FA_OK;
 }
 
 }  // namespace
@@ -168,6 +203,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* stream) {
     return bwd_common(true, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
                       dropout_p, seed, workspace, workspace_bytes_, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, uint64_t seed, void* stream) {
+    const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dropout_p);
+    if (st != FA_OK) return st;
+    if (workspace_bytes(B, H, N, d) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_INVALID_ARG;
+    void* ws = nullptr;
+    const int sst = scratch_for_current_device(&ws);
+    if (sst != FA_OK) return sst;
+    return bwd_common(true, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                      dropout_p, seed, ws, FA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int fa_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,

@@ -114,8 +114,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * is regenerated a second time from the same Philox counters) and sums each
  * dQ row's key tiles in a fixed order, instead of fp32 atomics. dK and dV are
  * the same bits fa_bwd writes; without dropout so is dQ (fa_bwd takes this
- * path then). (Dao, FlashAttention-2, section 3.1.2: the
- * backward computes dQ from the same recomputed dS that gives dK and dV.)
+ * path then). The gradients are those of the forward, computed in fused
+ * kernels ("DL0056 FlashAttention", point (3)) from score and probability
+ * blocks recomputed rather than stored (inferensys glossary "FlashAttention",
+ * paragraph on recomputation); that dQ may come from a pass of its own over
+ * the same recomputed dS is this library's reading of those passages.
  */
 int fa_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -140,6 +143,27 @@ int fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  * Returns 0 if an argument is out of range.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd with
+ * the same arguments, result and validation, but no workspace argument. Its
+ * scratch (the same fp32 dQ accumulator, D and log2-unit LSE as fa_bwd's
+ * workspace) is a device array of FA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU it runs on, held until the process ends; the call itself
+ * allocates nothing. Problems whose fa_bwd_workspace_size exceeds
+ * FA_NOALLOC_SCRATCH_BYTES return FA_ERR_INVALID_ARG (for d = 64 that is
+ * B*H*N up to 508 000 rows, for d = 128 up to 258 000). Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls ordered on
+ * one stream, or synchronised, are safe. The first call on a device looks up
+ * the array's device address (FA_ERR_HIP if that fails).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, uint64_t seed, void* stream);
 
 /*
  * General layouts, element types, head sizes and variable-length batches.

@@ -34,6 +34,27 @@ def test_exports_every_declared_symbol(L):
         assert isinstance(getattr(L, name), ctypes._CFuncPtr)
 
 
+def test_noalloc_rejects_invalid_arguments(L):
+    """fa_bwd_noalloc validates like fa_bwd, and rejects a problem whose workspace
+    would not fit its scratch, all before any HIP call."""
+    inv, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    assert fa.NOALLOC_SCRATCH_BYTES == 128 << 20
+
+    def call(B=1, H=2, N=100, d=64, ptr=FAKE, scale=0.125, p=0.0):
+        return L.fa_bwd_noalloc(*([ptr] * 9), B, H, N, d, scale, 1, p, 0, None)
+    assert call(ptr=None) == inv
+    assert call(ptr=FAKE + 8) == inv
+    assert call(d=96) == uns
+    assert call(N=0) == inv
+    assert call(scale=float("nan")) == inv
+    assert call(p=1.0) == inv
+    # B*H*N rows: the largest that fits the scratch at d = 128, and one past it
+    rows_fit = max(r for r in range(258000, 258200) if L.fa_bwd_workspace_size(1, 1, r, 128) <= fa.NOALLOC_SCRATCH_BYTES)
+    assert L.fa_bwd_workspace_size(1, 1, rows_fit + 1, 128) > fa.NOALLOC_SCRATCH_BYTES
+    assert call(B=1, H=1, N=rows_fit + 1, d=128) == inv
+    assert call(B=2, H=32, N=8192, d=128) == inv
+
+
 def test_status_strings(L):
     for code in range(4):
         assert L.fa_status_string(code).startswith(b"FA_")
