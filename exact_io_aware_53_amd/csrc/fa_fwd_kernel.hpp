@@ -224,8 +224,10 @@ void fwd_kernel(FwdParams p) {
             const int buf = t & 1;
             wait_vmem();
             __syncthreads();
-            if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
-            if (t >= ntiles_w) continue;               // whole tile above this wave's diagonal
+            if (t >= ntiles_w) {                       // whole tile above this wave's diagonal
+                if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+                continue;
+            }
 
             const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * K_TILE;
             const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * V_TILE;
@@ -253,6 +255,10 @@ void fwd_kernel(FwdParams p) {
                 }
             }
 
+            // The next tile's copies go out after this tile's score products: the
+            // issuing wave stalls on its vector-memory instructions, and here that
+            // stall delays only vector work instead of the products' operand reads.
+            if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
             V8 pb[RB][NC];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
