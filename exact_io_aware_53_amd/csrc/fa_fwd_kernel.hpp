@@ -50,23 +50,16 @@
 namespace fa {
 namespace {
 
-// Without dropout, the exponentials of a tile are taken against the reference
-// maximum m2 of the tiles before it, without first finding the tile's own
-// maximum: every factor exp2(m2) cancels in O~ / l, so the result does not
-// depend on which reference is used as long as nothing overflows. The fp32 row
-// sum l, which the softmax forms anyway, watches for that: once a lane's share
-// of l reaches SUM_LIMIT (or is inf / NaN, as on the first tile, where
-// m2 = -inf), the tile is redone from its scores against the true running
-// maximum, with l, lb and O~ rescaled to it. Weights therefore stay below 2^20
-// and sums below 2^21, far inside fp32 and bf16 range, and the common path
-// spends no instructions on the row maximum. With dropout the scores cannot
-// stay live for a second pass without spilling (the generator needs the
-// registers), so those kernels find the maximum first and move the reference
-// once it is exceeded by DROPOUT_SLACK. To keep the dominant term of a peaked
-// row free of bf16 rounding error, O~ is normalised by the sum of the same
-// bf16-rounded weights it accumulated (lb); the fp32 sum (l) gives the
-// log-sum-exp.
-constexpr float SUM_LIMIT = 1048576.0f;   // 2^20
+// Without dropout the softmax keeps the exact running maximum: each tile's row
+// maximum is found first (in-lane max3 and one v_permlane32_swap) and moves the
+// reference, rescaling O~ and l, whenever it grows. The largest weight of a
+// row is then exactly 1 in bf16, so the dominant term of a peaked row carries
+// no rounding of its weight, and O~ is divided by the fp32 row sum l itself
+// (the same l that gives the log-sum-exp). With dropout the scores cannot stay
+// live for a second look without spilling (the generator needs the registers),
+// so those kernels move the reference only once it is exceeded by
+// DROPOUT_SLACK, and divide O~ by the sum of the same bf16-rounded weights it
+// accumulated (lb), which keeps a dominant weight's rounding out of O.
 constexpr float DROPOUT_SLACK = 8.0f;     // log2 units
 
 // LDS operand reads kept in flight ahead of the matrix-core product that uses them.
@@ -292,7 +285,7 @@ void fwd_kernel(FwdParams p) {
                             V2 w;
                             w[0] = (T)x0;
                             w[1] = (T)x1;
-                            lbf[rb] = dot2(w, ones, lbf[rb]);
+                            if constexpr (DROPOUT) lbf[rb] = dot2(w, ones, lbf[rb]);
                             if (DROPOUT) {
                                 w[0] = (T)((keep[kb] >> r) & 1u ? x0 : 0.0f);
                                 w[1] = (T)((keep[kb] >> (r + 1)) & 1u ? x1 : 0.0f);
@@ -343,13 +336,25 @@ void fwd_kernel(FwdParams p) {
                     }
                     weights(keep);
                 } else {
-                    const float l0 = lsum[rb], lb0 = lbf[rb];
-                    weights(nullptr);
-                    if (__builtin_amdgcn_ballot_w64(!(lsum[rb] < SUM_LIMIT))) {
-                        // a weight outgrew the reference: redo the tile against the maximum
-                        to_max(l0, lb0);
-                        weights(nullptr);
+                    // exact running maximum: move the reference whenever a row's maximum grows
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+                    const float mxc = max_with_partner32(mx) * p.sl2;
+                    if (__builtin_amdgcn_ballot_w64(mxc > m2[rb])) {
+                        const float m_new = fmaxf(m2[rb], mxc);
+                        // exp2(-inf) = 0 on a row's first tile; a row with no visible key keeps 1
+                        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m2[rb] - m_new);
+                        lsum[rb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+                        m2[rb] = m_new;
                     }
+                    weights(nullptr);
                 }
             }
 
@@ -370,12 +375,12 @@ void fwd_kernel(FwdParams p) {
             }
         }
 
-        // ---- epilogue: O = O~ / (lb (1 - p)), LSE = (m2 + log2 l) ln 2
+        // ---- epilogue: O = O~ / (l (1 - p)) (lb with dropout), LSE = (m2 + log2 l) ln 2
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int my_q = qw + 32 * rb + l32;
             const float ltot = add_with_partner32(lsum[rb]);
-            const float lbtot = add_with_partner32(lbf[rb]);
+            const float lbtot = DROPOUT ? add_with_partner32(lbf[rb]) : ltot;
             const float inv = p.inv_keep / lbtot;
             if (my_q < N) {
                 T* orow = oh + (size_t)my_q * ldo;

@@ -18,10 +18,10 @@ A second reading applies only to the wide-score stress tests (Q x16, a score
 range four times wider than any workload's): there rows often mix two or three
 keys of comparable weight, and the matrix-core product P~ V takes P~ in bf16.
 Each weight then carries a relative rounding error of up to 2^-8, which moves
-O_ic by up to 2^-8 sum_j W_ij |V_jc - O_ic| to first order (W = P o Z/(1-p),
-the weights that form O), on top of the storage rounding. An element of those
-tests that misses the plain bar must lie within that bound, computed from the
-oracle's own probabilities (p_rounding_bound); the report counts such elements.
+O by a first-order amount that p_rounding_bound computes from the oracle's own
+probabilities for the forward's arithmetic (see there), on top of the storage
+rounding. An element of those tests that misses the plain bar must lie within
+that bound; the report counts such elements.
 
 Every check appends one line to REPORT: the raw max |O - O_ref|, the largest
 |O_ref|, how many elements needed the storage allowance (|O_ref| >= 4 and
@@ -93,24 +93,31 @@ class Stats:
 
 
 def p_rounding_bound(q, k, v, o_ref, lse_ref, scale, causal, p, seed, b, h, rows=None):
-    """First-order bound of the bf16 P~ rounding, per element of O.
+    """First-order bound of the bf16 rounding of the weights P~, per element of O.
 
-    The kernel forms O_i = sum_j b_j Z_ij V_j / ((1-p) sum_j b_j) from weights b_j
-    = w_j (1 + e_j), |e_j| <= 2^-8, the denominator summing every weight (dropped
-    ones too). To first order O moves by sum_j P_ij e_j (Z_ij V_j / (1-p) - O_i),
-    so |error| <= 2^-8 sum_j P_ij |Z_ij V_jc / (1-p) - O_ic|. P is taken from the
-    oracle's scores and log-sum-exp (fp64 arrays of one head; `rows` as given to
-    the oracle)."""
+    Each weight enters the product rounded, b_j = w_j (1 + e_j) with |e_j| <= 2^-8.
+    * Without dropout the forward keeps the exact running maximum, so the row's
+      largest weight is exactly 1 (e = 0), and divides by the fp32 sum of the
+      unrounded weights: O_i moves by sum_j P_ij e_j V_j, so
+      |error| <= 2^-8 sum over keys other than the row's maximum of P_ij |V_jc|.
+    * With dropout it divides by the sum of the rounded weights (dropped ones
+      included): O_i moves by sum_j P_ij e_j (Z_ij V_j / (1-p) - O_i), so
+      |error| <= 2^-8 sum_j P_ij |Z_ij V_jc / (1-p) - O_ic|.
+    P comes from the oracle's scores and log-sum-exp (fp64 arrays of one head;
+    `rows` as given to the oracle)."""
     import oracle
     s = oracle.scores(q, k, scale, causal, rows)
     with np.errstate(under="ignore"):
         prob = np.exp(s - np.asarray(lse_ref)[:, None])
     rr = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-    keep = (oracle.keep_mask(b, h, rr, np.arange(k.shape[0]), p, seed) / (1.0 - float(np.float32(p)))
-            if p > 0.0 else None)
     v = np.asarray(v, np.float64)
     bound = np.empty_like(np.asarray(o_ref))
-    for i in range(prob.shape[0]):
-        vi = v if keep is None else keep[i][:, None] * v
-        bound[i] = prob[i] @ np.abs(vi - o_ref[i][None, :])
+    if p > 0.0:
+        keep = oracle.keep_mask(b, h, rr, np.arange(k.shape[0]), p, seed) / (1.0 - float(np.float32(p)))
+        for i in range(prob.shape[0]):
+            bound[i] = prob[i] @ np.abs(keep[i][:, None] * v - o_ref[i][None, :])
+    else:
+        for i in range(prob.shape[0]):
+            w = np.where(s[i] < s[i].max(), prob[i], 0.0)
+            bound[i] = w @ np.abs(v)
     return 2.0 ** -8 * bound
