@@ -45,6 +45,14 @@ FWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_fwd.hip", "exact_io_aware_53_amd/c
 
 DECODE_SOURCES = ["exact_io_aware_53_amd/csrc/fa_decode_bf16.hip", "exact_io_aware_53_amd/csrc/fa_device.hpp",
                   "exact_io_aware_53_amd/csrc/fa_tiles.hpp", "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
+BWD_SOURCES = ["exact_io_aware_53_amd/csrc/fa_bwd.hip", "exact_io_aware_53_amd/csrc/fa_bwd_kernels.hpp",
+               "exact_io_aware_53_amd/csrc/fa_bwd_dq.hpp", "exact_io_aware_53_amd/csrc/fa_device.hpp",
+               "exact_io_aware_53_amd/csrc/fa_tiles.hpp", "exact_io_aware_53_amd/csrc/fa_launch.hpp"]
+# Vector-instruction issue ceiling: a full-rate wave64 VALU instruction (fp32 add, fma,
+# integer add/xor) occupies a SIMD's 16 lanes for 4 cycles, so 1024 SIMDs at 2.4 GHz issue
+# at most 614.4e9 of them per second (the fp32 vector peak 157.3 TFLOP/s is the same figure
+# times 64 lanes x 2 FLOP per FMA x 2 for packed pairs, which these kernels do not use).
+PEAK_VALU_GINSTR = 614.4
 
 
 def source_hash(paths):
@@ -90,6 +98,33 @@ def counter_traffic(workload_name):
         return None
 
 
+def profile_fields(name, sources):
+    """The `- key: value` fields of a committed counter summary under profiles/, or {}
+    when it is absent or its kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return {}
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", open(path).read(), flags=re.M))
+    if fields.get("source_hash") != source_hash(sources):
+        return {}
+    return {k: float(v) for k, v in fields.items() if k != "source_hash"}
+
+
+def mfma_roofline(flops, ms, traffic=None):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+
+def valu_roofline(instr, ms, what):
+    """Issue rate of the launch's vector instructions (from the committed counters)."""
+    if instr is None:
+        return None
+    g = instr / (ms * 1e-3) / 1e9
+    return {"bound": "alu", "achieved": round(g, 1), "peak": PEAK_VALU_GINSTR, "unit": "G VALU instr/s",
+            "frac": round(g / PEAK_VALU_GINSTR, 4), "work": what}
+
+
 def time_launches(fn, steps, warmup, stream):
     """Run fn warmup times, then `steps` timed times; returns (wall ms/step, per-launch event ms)."""
     import torch
@@ -133,10 +168,14 @@ def cpu_baseline(w, inputs, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    executed = 4.0 * rows_done * w.N * w.d       # the oracle forms every key's score and masks
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{heads_done} of {w.B * w.H} heads ({rows_done} query rows, all keys) of "
-                      f"{w.name}, fp64 NumPy, {dt:.1f} s; FLOPs counted as for the GPU"}
+            "executed_tflops": round(executed / dt / 1e12, 6),
+            "sample": f"{heads_done} of {w.B * w.H} heads ({rows_done} query rows) of {w.name}, "
+                      f"fp64 NumPy, {dt:.1f} s. The oracle forms dense score rows (every key, then the "
+                      f"causal mask), {executed / max(flops, 1):.2f}x the FLOPs it is credited with: value "
+                      f"counts 4*N^2*d/2 per causal head as for the GPU; executed_tflops counts what it ran"}
 
 
 def main():
@@ -252,6 +291,18 @@ def main():
             "ms_bwd_deterministic": round(td, 4),
             "tflops_bwd_deterministic": round(w2.bwd_flops() / (td * 1e-3) / 1e12, 3),
         }
+        # Philox-bound: vector-instruction issue against its ceiling (counts from the
+        # committed counters), with the matrix-core fraction beside it.
+        pf = profile_fields(f"fa_fwd_bf16_{w2.name}_counters.md", FWD_SOURCES)
+        pb = profile_fields(f"fa_bwd_bf16_{w2.name}_counters.md", BWD_SOURCES)
+        line["fwd_bwd"]["roofline_fwd"] = valu_roofline(
+            pf.get("valu_instr_per_launch"), tf, "softmax and one Philox-4x32-10 call per unmasked score")
+        line["fwd_bwd"]["roofline_bwd"] = valu_roofline(
+            pb.get("fused_valu_instr_per_call"), tb, "recompute, one Philox call per unmasked score, five products")
+        line["fwd_bwd"]["roofline_bwd_deterministic"] = valu_roofline(
+            pb.get("det_valu_instr_per_call"), td, "as the fused form, with the Philox calls made in both passes")
+        line["fwd_bwd"]["mfma_fwd"] = mfma_roofline(w2.fwd_flops(), tf, pf.get("hbm_bytes_per_launch"))
+        line["fwd_bwd"]["mfma_bwd"] = mfma_roofline(w2.bwd_flops(), tb, pb.get("fused_hbm_bytes_per_call"))
         del q2, k2, v2, do2, o2, l2, dq2, dk2, dv2, ws
 
         # The backward at the forward workload's shape (no dropout: the two-pass
@@ -268,9 +319,11 @@ def main():
                    seed=w.dropout_seed, dq=dq3, dk=dk3, dv=dv3, workspace=ws3)
 
         t3, _ = time_launches(b3, args.steps, args.warmup, stream)
+        p3 = profile_fields(f"fa_bwd_bf16_b{w.B}h{w.H}n{w.N}d{w.d}_counters.md", BWD_SOURCES)
         line["bwd"] = {"workload": w.name, "ms_bwd": round(t3, 4),
                        "tflops_bwd": round(w.bwd_flops() / (t3 * 1e-3) / 1e12, 3),
-                       "frac": round(w.bwd_flops() / (t3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                       "frac": round(w.bwd_flops() / (t3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "roofline": mfma_roofline(w.bwd_flops(), t3, p3.get("hbm_bytes_per_call"))}
         del do3, dq3, dk3, dv3, ws3
 
     if not args.no_long:
@@ -326,8 +379,16 @@ def main():
 
             _, evo = time_launches(fo, args.steps, args.warmup, stream)
             mo = sum(evo) / len(evo)
-            others.append({"workload": name, "dtype": wo.dtype, "us": round(mo * 1e3, 2),
-                           "tflops": round(wo.fwd_flops() / (mo * 1e-3) / 1e12, 3)})
+            entry = {"workload": name, "dtype": wo.dtype, "us": round(mo * 1e3, 2),
+                     "tflops": round(wo.fwd_flops() / (mo * 1e-3) / 1e12, 3)}
+            if wo.dtype == "bf16":
+                po = profile_fields(f"fa_fwd_bf16_{name}_counters.md", FWD_SOURCES)
+                entry["roofline"] = mfma_roofline(wo.fwd_flops(), mo, po.get("hbm_bytes_per_launch"))
+                entry["valu"] = valu_roofline(po.get("valu_instr_per_launch"), mo,
+                                              "softmax: fma, exp2, add, half a cvt and half a max3 per score")
+            else:
+                entry["bound"] = "launch latency (one 128-row head, 8 workgroups)"
+            others.append(entry)
             del qo, ko, vo, oo, lo
         line["other_configs"] = others
 
