@@ -33,7 +33,9 @@
 //   access shapes, row operands and transposed reads, are conflict-free.
 // * Two-pass form (DQ = false): the same kernel without the dQ products, then
 //   bwd_dq_kernel for dQ. No atomics, so bitwise deterministic; without
-//   dropout it is also the faster form and the default.
+//   dropout it is also the faster form and the default. At d = 128 its key
+//   side is bwd_kv_split_kernel: the work of each 32 keys split between two
+//   waves of one SIMD.
 // * Layouts as in the forward: per-tensor batch/head/row strides, packed
 //   variable-length sequences. Head sizes 32 and 96 run the kernels of 64 and
 //   128 on rows padded with zeros (DH = the stored width, D = the computed
@@ -44,18 +46,23 @@
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
-// Key-side two-pass kernel at d = 128: dK^T and dV^T accumulate in AGPRs.
-#ifndef FA_KV_AGPR
-#define FA_KV_AGPR 1
-#endif
 #ifndef FA_KV_PF
 #define FA_KV_PF 2
 #endif
 #ifndef FA_KV_TF
 #define FA_KV_TF 2
+#endif
+// Operand reads in flight ahead of the products of the split key side (d = 128).
+#ifndef FA_KVS_PF
+#define FA_KVS_PF 2
+#endif
+#ifndef FA_KVS_TF
+#define FA_KVS_TF 2
 #endif
 
 constexpr int kBKV = 128;     // keys per workgroup
@@ -122,9 +129,6 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     constexpr int NBUF = DQ ? 1 : 2;   // Q/dO tile buffers
     // LDS operand pairs in flight ahead of their products (S/dP, then dV/dK).
     constexpr int kPf = D == 256 ? 1 : FA_KV_PF, kTf = D == 256 ? 1 : FA_KV_TF;
-    // d = 128, two-pass form: dK^T and dV^T accumulate in AGPRs through inline
-    // products, leaving the VGPRs to K, V, the score tile and the operand rings.
-    constexpr bool kAgpr = FA_KV_AGPR && D == 128 && !DQ;
     __shared__ __attribute__((aligned(1024))) char q_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NBUF * TILE];
     __shared__ __attribute__((aligned(1024))) char k_s[DQ ? kBKV * D * 2 : 16];
@@ -266,10 +270,10 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
         const float* const lse_t = lse_s + buf * 64;
         const float* const dsum_t = dsum_s + buf * 64;
 
-        // Every query of the tile precedes our keys. (d = 256, and dK/dV in AGPRs,
-        // run such tiles fully masked instead: their zero contributions cost
-        // less than the register copies a second path through the loop costs.)
-        const bool skip = CAUSAL && D != 256 && !kAgpr && kw > i0 + BQ - 1;
+        // Every query of the tile precedes our keys. (d = 256 runs such tiles
+        // fully masked instead: their zero contributions cost less than the
+        // register copies a second path through the loop costs.)
+        const bool skip = CAUSAL && D != 256 && kw > i0 + BQ - 1;
         if (skip) {
             // this wave's rows of dS^T are zero for this tile
             if constexpr (DQ)
@@ -365,13 +369,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
                 for (int j = 0; j < TI; ++j) {
                     const int qc = j / DB, db = j % DB;
-                    if constexpr (kAgpr) {
-                        mfma_agpr(dva[db], oa[j % kTf], bp[qc & 1]);
-                        mfma_agpr(dka[db], ta[j % kTf], bs[qc & 1]);
-                    } else {
-                        dva[db] = mfma32(oa[j % kTf], bp[qc & 1], dva[db]);
-                        dka[db] = mfma32(ta[j % kTf], bs[qc & 1], dka[db]);
-                    }
+                    dva[db] = mfma32(oa[j % kTf], bp[qc & 1], dva[db]);
+                    dka[db] = mfma32(ta[j % kTf], bs[qc & 1], dka[db]);
                     if (j + kTf < TI) {
                         oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
                         ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
@@ -460,13 +459,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                                 bs[i] = (T)dp[qc >> 1][8 * (qc & 1) + i];
                             }
                         }
-                        if constexpr (kAgpr) {
-                            mfma_agpr(dva[db], oa[j % kTf], bp);
-                            mfma_agpr(dka[db], ta[j % kTf], bs);
-                        } else {
-                            dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
-                            dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
-                        }
+                        dva[db] = mfma32(oa[j % kTf], bp, dva[db]);
+                        dka[db] = mfma32(ta[j % kTf], bs, dka[db]);
                         if (j + kTf < TI) {
                             oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
                             ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
@@ -512,13 +506,6 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     }
 
     // dK = s dK^T, dV = dV^T, transposed on the way out (lane = key, registers = d)
-    if constexpr (kAgpr) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            settle(dka[db]);
-            settle(dva[db]);
-        }
-    }
     if (my_key < N) {
         T* dkr = (T*)p.dk + p.ldk.base(b, h, start) + (size_t)my_key * p.ldk.sn;
         T* dvr = (T*)p.dv + p.ldv.base(b, h, start) + (size_t)my_key * p.ldv.sn;
@@ -535,6 +522,325 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
                 }
                 *(V4*)(dkr + 32 * db + 8 * g + 4 * hi) = wk;
                 *(V4*)(dvr + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+        }
+    }
+}
+
+// Key-side pass of the two-pass form at d = 64 and 128 with the work of 32
+// keys split between two waves on one SIMD (8 waves, 128 keys per workgroup).
+// Wave p (p < 4) takes the P side: S = Q K^T, P = exp(S - LSE), and
+// dV^T += dO^T (P Z'). Wave p + 4, on the same SIMD, takes the dS side:
+// dP = dO V^T, dS = P (dP Z' - D), and dK^T += Q^T dS. Each wave then holds one
+// operand block and one accumulator pair (K or V, dV^T or dK^T), which fits the
+// 256 registers of a lane at two waves per SIMD, and each SIMD always has a
+// second wave whose products run while the first does vector work or waits for
+// LDS. P crosses from the P side to the dS side through LDS in fp32 (its sign
+// bit carries the dropout decision Z = 0), one tile late: in iteration t the dS
+// side forms dS and the dK products of tile t - 1 while both sides run the
+// products of tile t, so one barrier per tile orders everything. Q tiles are
+// kept three deep (t - 1 for dK, t, t + 1 arriving), dO tiles two deep. The
+// arithmetic of every element and the order of every accumulation are those of
+// bwd_kv_kernel, so dK and dV are bit-identical to it.
+template <typename T, int D, int DH, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p) {
+    using V8 = typename Vec<T>::x8;
+    constexpr int NW = 2 * kNW;                      // waves per workgroup
+    constexpr int BQ = 64, QB = 2, CH = D / 8, DB = D / 32, NCD = D / 16;
+    constexpr int TILE = BQ * D * 2, ROW = D * 2;
+    constexpr int QLOADS = BQ * CH / (64 * kNW);     // copies per dS-side wave and tensor
+    constexpr int NQ = 3, NO = 2;                    // Q and dO tile buffers
+    constexpr int XF = kNW * QB * 16 * 64;           // floats of P per exchange buffer
+    constexpr int kPf = FA_KVS_PF, kTf = FA_KVS_TF;
+    constexpr int SI = QB * NCD;                     // score products per wave and tile
+    constexpr int TI = (BQ / 16) * DB;               // dV or dK products per wave and tile
+    static_assert(D == 64 || D == 128, "d = 64 or 128");
+    static_assert(QLOADS >= 1 && QLOADS * 64 * kNW == BQ * CH, "copies split over the dS-side waves");
+    __shared__ __attribute__((aligned(1024))) char q_s[NQ * TILE];
+    __shared__ __attribute__((aligned(1024))) char do_s[NO * TILE];
+    __shared__ __attribute__((aligned(16))) float x_s[2 * XF];
+    __shared__ __attribute__((aligned(16))) float lse_s[NQ * 64];
+    __shared__ __attribute__((aligned(16))) float dsum_s[NQ * 64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = wave & 3;                       // key slice; waves pair and pair + 4 share a SIMD
+    const bool dside = wave >= kNW;
+    const int l32 = lane & 31, hi = lane >> 5;
+    FA_LDS char* const qL = (FA_LDS char*)q_s;
+    FA_LDS char* const doL = (FA_LDS char*)do_s;
+
+    int bh, kb;
+    const int bid = blockIdx.x;
+    if ((p.heads & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3;
+        bh = (slot / p.nkb) * 8 + xcd;
+        kb = slot % p.nkb;
+    } else {
+        bh = bid % p.heads;
+        kb = bid / p.heads;
+    }
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    const int b = bh / p.H, h = bh - b * p.H;
+    int start, N;
+    sequence(p.cu, p.total, p.N, b, start, N);
+    const int j0 = kb * kBKV;
+    if (j0 >= N) return;
+    const int ldq = p.lq.sn, ldk = p.lk.sn, ldv = p.lv.sn, ldo = p.ldo.sn;
+    const T* const qh = (const T*)p.q + p.lq.base(b, h, start);
+    const T* const kh = (const T*)p.k + p.lk.base(b, h, start);
+    const T* const vh = (const T*)p.v + p.lv.base(b, h, start);
+    const T* const doh = (const T*)p.dout + p.ldo.base(b, h, start);
+    const auto rs_q = make_rsrc(qh, (uint32_t)(((size_t)(N - 1) * ldq + DH) * 2));
+    const auto rs_k = make_rsrc(kh, (uint32_t)(((size_t)(N - 1) * ldk + DH) * 2));
+    const auto rs_v = make_rsrc(vh, (uint32_t)(((size_t)(N - 1) * ldv + DH) * 2));
+    const auto rs_do = make_rsrc(doh, (uint32_t)(((size_t)(N - 1) * ldo + DH) * 2));
+    const size_t wrow = (size_t)bh * p.N;
+    const auto rs_lse = make_rsrc(p.lse2 + wrow, (uint32_t)N * 4);
+    const auto rs_ds = make_rsrc(p.dsum + wrow, (uint32_t)N * 4);
+
+    const int kw = j0 + pair * 32;
+    const int my_key = kw + l32;
+    const PhiloxCol philox_col((uint32_t)b, (uint32_t)h, (uint32_t)my_key, p.key);
+
+    // Operand offsets as in bwd_kv_kernel.
+    const int grp = lane >> 4, sl = lane & 15;
+    const int tr_row = 4 * (grp >> 1) + (sl >> 2), tr_col = 16 * (grp & 1) + 4 * (sl & 3);
+    int roff[NCD], troff[DB][2];
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) roff[c] = tile_offset<CH>(l32, 16 * c + 8 * hi);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) troff[db][half] = tile_offset<CH>(tr_row + 8 * half, 32 * db + tr_col);
+    auto so = [&](int i) { return roff[i / QB] + (i % QB) * 32 * ROW; };       // score step i: chunk i/QB, block i%QB
+    auto to = [&](int j, int half) { return troff[j % DB][half] + 16 * (j / DB) * ROW; };
+
+    // K rows (P side) or V rows (dS side) of this pair's keys as B operands.
+    V8 kv[NCD];
+    {
+        const auto rs = dside ? rs_v : rs_k;
+        const int ld = dside ? ldv : ldk;
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) kv[c] = __builtin_bit_cast(V8, buffer_load16(rs, chunk_src<DH>(my_key, 2 * c + hi, ld)));
+    }
+    f32x16 acc[DB];                 // dV^T (P side) or dK^T (dS side)
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    f32x16 sc[QB];                  // S (P side) or dP of the previous tile (dS side)
+    V8 bop[BQ / 16];                // P Z' (P side) or dS (dS side), bf16 B operands
+
+    // Copies of tile i0: QLOADS Q chunks and QLOADS dO chunks per dS-side wave,
+    // and one row-term copy (LSE by even pairs, D by odd ones).
+    // The dS side issues every copy: it starts each tile with vector work, so
+    // the time the copies take to issue does not hold up the S products.
+    auto issue_tile = [&](int i0, int t) __attribute__((always_inline)) {
+        const int qbuf = t % NQ, obuf = t % NO;
+#pragma unroll
+        for (int i = 0; i < QLOADS; ++i) {
+            const int blk = i * kNW + pair, pos = blk * 64 + lane;
+            const int row = pos / CH, ch = (pos % CH) ^ chunk_swizzle<CH>(row);
+            buffer_to_lds16_async(rs_q, (FA_LDS void*)(qL + qbuf * TILE + blk * 1024), chunk_src<DH>(i0 + row, ch, ldq));
+            buffer_to_lds16_async(rs_do, (FA_LDS void*)(doL + obuf * TILE + blk * 1024),
+                                  chunk_src<DH>(i0 + row, ch, ldo));
+        }
+        if (pair & 1)
+            buffer_to_lds4_async(rs_ds, (FA_LDS void*)(dsum_s + qbuf * 64), (uint32_t)(i0 + lane) * 4);
+        else
+            buffer_to_lds4_async(rs_lse, (FA_LDS void*)(lse_s + qbuf * 64), (uint32_t)(i0 + lane) * 4);
+    };
+
+    // dS of tile t (from dP in sc, P from exchange buffer t % 2, D from slot
+    // t % NQ) into bop, then dK^T += Q^T dS over Q buffer t % NQ. The dP
+    // products of the next tile, if any (NEXT), are interleaved with the dK
+    // products.
+    auto ds_side = [&](int t, auto next, int tn) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next)::value;
+        const float* const dsum_t = dsum_s + (t % NQ) * 64;
+        const float* const xp = x_s + (t & 1) * XF + pair * QB * 16 * 64;
+        // group n = 4qb + g: elements r = 4g .. 4g + 3 of block qb; its P and D
+        // are read one group ahead
+        auto xo = [&](int n) { return xp + (n * 64 + lane) * 4; };
+        auto dof = [&](int n) { return dsum_t + (n >> 2) * 32 + 8 * (n & 3) + 4 * hi; };
+        f32x4 xr = *(const f32x4*)xo(0), dr = *(const f32x4*)dof(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < QB * 4; ++n) {
+            const int qb = n >> 2, g = n & 3;
+            const f32x4 x = xr, dd = dr;
+            if (n + 1 < QB * 4) {
+                xr = *(const f32x4*)xo(n + 1);
+                dr = *(const f32x4*)dof(n + 1);
+            }
+            float ds[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float pr = x[u], z = 1.0f;
+                if (DROPOUT) {
+                    const uint32_t bits = __float_as_uint(x[u]);
+                    z = (bits >> 31) ? 0.0f : p.inv_keep;
+                    pr = __uint_as_float(bits & 0x7fffffffu);
+                }
+                ds[u] = pr * fmaf(sc[qb][4 * g + u], z, -dd[u]);
+            }
+            // element r = 4g + u of block qb is element 8(qc & 1) + i of chunk qc = 2qb + g/2
+            const int qc = 2 * qb + (g >> 1), i = 4 * (g & 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bop[qc][i + u] = (T)ds[u];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const FA_LDS char* const qT = qL + (t % NQ) * TILE;
+        const FA_LDS char* const doN = doL + (tn % NO) * TILE;
+        V8 ta[kTf], da[kPf];
+#pragma unroll
+        for (int j = 0; j < kTf; ++j) ta[j] = tr_read<V8>(qT, to(j, 0), to(j, 1));
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int j = 0; j < kPf; ++j) da[j] = *(const FA_LDS V8*)(doN + so(j));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_assert(TI == SI, "one dP product per dK product");
+#pragma unroll
+        for (int j = 0; j < TI; ++j) {
+            const int qc = j / DB, db = j % DB;
+            acc[db] = mfma32(ta[j % kTf], bop[qc], acc[db]);
+            if (j + kTf < TI) ta[j % kTf] = tr_read<V8>(qT, to(j + kTf, 0), to(j + kTf, 1));
+            if constexpr (NEXT) {
+                const int qb = j % QB, c = j / QB;
+                sc[qb] = mfma32(da[j % kPf], kv[c], c == 0 ? f32x16{} : sc[qb]);
+                if (j + kPf < SI) da[j % kPf] = *(const FA_LDS V8*)(doN + so(j + kPf));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int i_first = CAUSAL ? j0 : 0;
+    const int i_last = (N - 1) / BQ * BQ;
+    const int ntiles = (i_last - i_first) / BQ + 1;   // tile t starts at row i_last - t BQ
+    if (dside) issue_tile(i_last, 0);
+
+    // Each side runs a loop of its own (their loop-invariant values would
+    // otherwise all be live in one loop); both take the same barriers.
+    if (!dside) {
+        for (int t = 0; t < ntiles; ++t) {
+            const int i0 = i_last - t * BQ;
+            wait_vmem();
+            __syncthreads();
+            // ---- P side: S = Q K^T of tile t
+            const FA_LDS char* const qT = qL + (t % NQ) * TILE;
+            V8 qa[kPf];
+#pragma unroll
+            for (int j = 0; j < kPf; ++j) qa[j] = *(const FA_LDS V8*)(qT + so(j));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < SI; ++i) {
+                const int qb = i % QB, c = i / QB;
+                sc[qb] = mfma32(qa[i % kPf], kv[c], c == 0 ? f32x16{} : sc[qb]);
+                if (i + kPf < SI) qa[i % kPf] = *(const FA_LDS V8*)(qT + so(i + kPf));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
+                const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
+                const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int e = qb * 32 + 8 * (r >> 2) + (r & 3);
+                        if (e < e_lo || e >= e_hi) sc[qb][r] = -INFINITY;
+                    }
+            }
+            // P = exp2(s scale log2(e) - LSE_i log2(e)); P Z' into the dV operands,
+            // P (sign = dropped) to the dS side
+            const float* const lse_t = lse_s + (t % NQ) * 64;
+            float* const xp = x_s + (t & 1) * XF + pair * QB * 16 * 64;
+            auto lof = [&](int n) { return lse_t + (n >> 2) * 32 + 8 * (n & 3) + 4 * hi; };
+            f32x4 lr = *(const f32x4*)lof(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < QB * 4; ++n) {
+                const int qb = n >> 2, g = n & 3;
+                const f32x4 lv = lr;
+                if (n + 1 < QB * 4) lr = *(const f32x4*)lof(n + 1);
+                f32x4 x;
+                const int qc = 2 * qb + (g >> 1), i = 4 * (g & 1);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float pr = fast_exp2(fmaf(sc[qb][4 * g + u], p.sl2, -lv[u]));   // exp2(-inf) = 0
+                    float z = 1.0f;
+                    x[u] = pr;
+                    if (DROPOUT) {
+                        const int qrow = qb * 32 + 8 * g + 4 * hi + u;
+                        const bool keep = philox_col.word0((uint32_t)(i0 + qrow)) >= p.thr;
+                        z = keep ? p.inv_keep : 0.0f;
+                        x[u] = __uint_as_float(__float_as_uint(pr) | (keep ? 0u : 0x80000000u));
+                    }
+                    bop[qc][i + u] = (T)(pr * z);
+                }
+                *(f32x4*)(xp + (n * 64 + lane) * 4) = x;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // dV^T += dO^T (P Z') over tile t
+            const FA_LDS char* const doT = doL + (t % NO) * TILE;
+            V8 oa[kTf];
+#pragma unroll
+            for (int j = 0; j < kTf; ++j) oa[j] = tr_read<V8>(doT, to(j, 0), to(j, 1));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TI; ++j) {
+                const int qc = j / DB, db = j % DB;
+                acc[db] = mfma32(oa[j % kTf], bop[qc], acc[db]);
+                if (j + kTf < TI) oa[j % kTf] = tr_read<V8>(doT, to(j + kTf, 0), to(j + kTf, 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+    } else {
+        for (int t = 0; t < ntiles; ++t) {
+            const int i0 = i_last - t * BQ;
+            wait_vmem();
+            __syncthreads();
+            if (t + 1 < ntiles) issue_tile(i0 - BQ, t + 1);
+            // ---- dS side: dS and dK of tile t - 1, with the dP products of tile t
+            if (t == 0) {
+                const FA_LDS char* const doT = doL;
+                V8 da[kPf];
+#pragma unroll
+                for (int j = 0; j < kPf; ++j) da[j] = *(const FA_LDS V8*)(doT + so(j));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < SI; ++i) {
+                    const int qb = i % QB, c = i / QB;
+                    sc[qb] = mfma32(da[i % kPf], kv[c], c == 0 ? f32x16{} : sc[qb]);
+                    if (i + kPf < SI) da[i % kPf] = *(const FA_LDS V8*)(doT + so(i + kPf));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                ds_side(t - 1, std::true_type{}, t);
+            }
+        }
+        // the last tile's dS and dK (its P was written in the last iteration)
+        __syncthreads();
+        ds_side(ntiles - 1, std::false_type{}, 0);
+    }
+
+    if (my_key < N) {
+        using V4 = typename Vec<T>::x4;
+        const Strides& lo = dside ? p.ldk : p.ldv;
+        T* row = (T*)(dside ? p.dk : p.dv) + lo.base(b, h, start) + (size_t)my_key * lo.sn;
+        const float mul = dside ? p.scale : 1.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            if (32 * db >= DH) break;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (T)(dside ? acc[db][4 * g + i] * mul : acc[db][4 * g + i]);
+                *(V4*)(row + 32 * db + 8 * g + 4 * hi) = w;
             }
         }
     }
@@ -662,8 +968,13 @@ hipError_t launch_kv_cfg(const BwdArgs& a, hipStream_t st) {
     // d = 256: 32-row query tiles, so that K, V, dK, dV of a wave's 32 keys and
     // the score tile fit in the 512 registers of a lane.
     constexpr int BQ = D == 256 ? 32 : 64;
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, DH, BQ, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
-                       dim3(kNW * 64), 0, st, p);
+    // d = 128, two-pass form: the key side split over two waves per SIMD.
+    if constexpr (!DQ && D == 128)
+        hipLaunchKernelGGL((bwd_kv_split_kernel<T, D, DH, CAUSAL, DROPOUT>), dim3(p.heads * p.nkb),
+                           dim3(2 * kNW * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((bwd_kv_kernel<T, D, DH, BQ, CAUSAL, DROPOUT, DQ>), dim3(p.heads * p.nkb),
+                           dim3(kNW * 64), 0, st, p);
     return hipGetLastError();
 }
 

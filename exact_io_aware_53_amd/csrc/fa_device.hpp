@@ -52,22 +52,6 @@ __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// 32x32x16 product accumulating in AGPRs, for accumulators that only the
-// matrix core touches until an epilogue (it frees their VGPRs for the rest).
-// Inline assembly is invisible to the compiler's hazard checks, so two wait
-// states lead each product (its operands may have been written by vector
-// instructions just before) and settle() gives 24 before vector code reads
-// the accumulator.
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, f16x8 a, f16x8 b) {
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void settle(f32x16& acc) {
-    asm volatile("s_nop 7\n s_nop 7\n s_nop 7" : "+a"(acc));
-}
-
 #define FA_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;

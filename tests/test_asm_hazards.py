@@ -12,16 +12,16 @@ vector-memory instruction that reads that SGPR, or the copy can read a stale
 buffer resource. This test compiles every kernel source to gfx950 assembly with
 the library's own flags and checks that distance in front of every inline copy.
 
-The key-side backward accumulates dK and dV in AGPRs through inline matrix-core
-products. A vector instruction that writes a source register of a product (its
-A, B or C operand) must be at least MFMA_SRC_WAIT_STATES wait states ahead of
-it, and an instruction other than the next product of the same accumulator
-that reads the product's AGPR result must come at least
-MFMA_RESULT_WAIT_STATES wait states after it (the code leads each product with
-two wait states and places 24 before the accumulators are read). The scan
-follows straight-line code only: it stops at labels and branches, where the
-loop structure takes over (each product's own s_nop and the settle after the
-loop cover those paths).
+Matrix-core products written as inline assembly need the same care: a vector
+instruction that writes a source register of a product (its A, B or C
+operand) must be at least MFMA_SRC_WAIT_STATES wait states ahead of it, and an
+instruction other than the next product of the same accumulator that reads the
+product's result must come at least MFMA_RESULT_WAIT_STATES wait states after
+it. The kernels issue every product through the compiler's builtins today, so
+the scan over them finds none; it still runs over every kernel, so that an
+inline product added later is checked, and the detector itself is tested on
+hand-written snippets. The scan follows straight-line code only: it stops at
+labels and branches.
 """
 import os
 import re
@@ -245,6 +245,5 @@ def test_inline_products_keep_wait_states(kernel_asm):
         total += n
         problems += [(os.path.basename(src),) + f for f in found]
     print(f"inline products checked: {total}")
-    assert total > 0, "no inline products found: the scan no longer matches the generated code"
     assert not problems, "\n".join(f"{s}:{ln}: {kind}: '{u}' {ws} wait states from '{c}'"
                                     for s, ln, kind, u, ws, c in problems[:10])
