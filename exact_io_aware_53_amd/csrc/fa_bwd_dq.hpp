@@ -38,6 +38,7 @@ namespace {
 #define FA_DQ_TF 4
 #endif
 
+
 struct DqParams {
     const void* q;
     const void* k;
@@ -196,8 +197,10 @@ void bwd_dq_kernel(DqParams p) {
             const int buf = t & 1;
             wait_vmem();
             __syncthreads();
-            if (t + 1 < nt) issue(t + 1, buf ^ 1);
-            if (t >= Tw) continue;
+            if (t >= Tw) {
+                if (t + 1 < nt) issue(t + 1, buf ^ 1);
+                continue;
+            }
             const FA_LDS char* kt = (const FA_LDS char*)kbuf + buf * TILE;
             const FA_LDS char* vt = (const FA_LDS char*)vbuf + buf * TILE;
             const int k0 = t * BC;
@@ -228,6 +231,10 @@ void bwd_dq_kernel(DqParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            // The next tile's copies go out once this tile's score products are
+            // issued: issuing copies stalls the wave, and here that stall overlaps
+            // the products instead of delaying their first operand reads.
+            if (t + 1 < nt) issue(t + 1, buf ^ 1);
             // log2 P = s * scale * log2(e) - LSE_i * log2(e); masked elements -> -inf
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -314,9 +321,9 @@ void bwd_dq_kernel(DqParams p) {
     }
 }
 
-template <typename T, int D, int DH, bool CAUSAL, bool DROPOUT>
-hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t st) {
-    constexpr int BC = 64, NW = 4, BR = NW * 32;
+template <typename T, int D, int DH, int NW, bool CAUSAL, bool DROPOUT>
+hipError_t launch_dq_nw(const BwdArgs& a, hipStream_t st) {
+    constexpr int BC = 64, BR = NW * 32;
     DqParams p{};
     p.q = a.q;
     p.k = a.k;
@@ -345,6 +352,21 @@ hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, DH, BC, NW, CAUSAL, DROPOUT>), dim3(p.heads * blocks), dim3(NW * 64),
                        0, st, p);
     return hipGetLastError();
+}
+
+// Up to d = 128, eight waves (256 query rows) share each K/V tile when that
+// grid still has two workgroups per CU of the 256-CU device; otherwise four
+// (128 rows), which doubles the workgroups of small grids. Each row's
+// arithmetic is the same either way, so dQ is bit-identical. (d = 256 needs a
+// SIMD's whole register file per wave: four waves.)
+template <typename T, int D, int DH, bool CAUSAL, bool DROPOUT>
+hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t st) {
+    if constexpr (D <= 128) {
+        const int nqb8 = (a.s.N + 255) / 256;
+        const long long wg8 = (long long)a.s.B * a.s.H * (CAUSAL ? (nqb8 + 1) / 2 : nqb8);
+        if (wg8 >= 512) return launch_dq_nw<T, D, DH, 8, CAUSAL, DROPOUT>(a, st);
+    }
+    return launch_dq_nw<T, D, DH, 4, CAUSAL, DROPOUT>(a, st);
 }
 
 // The query-side pass of the two-pass backward: dQ only.

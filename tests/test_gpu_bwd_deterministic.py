@@ -89,6 +89,21 @@ def test_deterministic_backward_small(shape, causal, p):
     assert worst <= GRAD_TOL, f"grad err {worst:.3e}"
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.1])
+def test_dq_pass_eight_wave_grid(d, causal, p):
+    """B4 H32 N2000: the dQ pass's grid reaches 512 workgroups of eight waves, so
+    it runs 256-row query blocks (the smaller shapes above run 128-row ones),
+    with a ragged last block of 208 rows; two heads against the oracle."""
+    shape = (4, 32, 2000, d)
+    q, k, v, do = normal_tensors(shape, 7070 + d, 4, torch.bfloat16)
+    det, ato = run_both(q, k, v, do, causal, p, SEED)
+    assert torch.equal(det[1], ato[1]) and torch.equal(det[2], ato[2])
+    worst = check_heads(q, k, v, do, det, [(0, 0), (3, 31)], causal, p, SEED)
+    assert worst <= GRAD_TOL, f"grad err {worst:.3e}"
+
+
 def test_deterministic_dq_is_bitwise_repeatable():
     shape = (2, 4, 1000, 128)
     q, k, v, do = (t.cuda() for t in normal_tensors(shape, 5151, 4, torch.bfloat16))
