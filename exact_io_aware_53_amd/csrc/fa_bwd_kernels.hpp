@@ -555,6 +555,7 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
     constexpr int SI = QB * NCD;                     // score products per wave and tile
     constexpr int TI = (BQ / 16) * DB;               // dV or dK products per wave and tile
     static_assert(D == 64 || D == 128, "d = 64 or 128");
+    static_assert(QB * 4 <= SI, "the P side reads its LSE groups during the score products");
     static_assert(QLOADS >= 1 && QLOADS * 64 * kNW == BQ * CH, "copies split over the dS-side waves");
     __shared__ __attribute__((aligned(1024))) char q_s[NQ * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NO * TILE];
@@ -653,19 +654,21 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
             buffer_to_lds4_async(rs_lse, (FA_LDS void*)(lse_s + qbuf * 64), (uint32_t)(i0 + lane) * 4);
     };
 
+    // LSE or D of tile t, group n = 4qb + g: rows 32qb + 8g + 4hi .. +3, the
+    // elements r = 4g .. 4g + 3 of score block qb.
+    auto row_terms = [&](const float* base, int t, int n) {
+        return *(const f32x4*)(base + (t % NQ) * 64 + (n >> 2) * 32 + 8 * (n & 3) + 4 * hi);
+    };
     // dS of tile t (from dP in sc, P from exchange buffer t % 2, D from slot
     // t % NQ) into bop, then dK^T += Q^T dS over Q buffer t % NQ. The dP
     // products of the next tile, if any (NEXT), are interleaved with the dK
     // products.
     auto ds_side = [&](int t, auto next, int tn) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
-        const float* const dsum_t = dsum_s + (t % NQ) * 64;
         const float* const xp = x_s + (t & 1) * XF + pair * QB * 16 * 64;
-        // group n = 4qb + g: elements r = 4g .. 4g + 3 of block qb; its P and D
-        // are read one group ahead
+        // group n: its P and D are read one group ahead
         auto xo = [&](int n) { return xp + (n * 64 + lane) * 4; };
-        auto dof = [&](int n) { return dsum_t + (n >> 2) * 32 + 8 * (n & 3) + 4 * hi; };
-        f32x4 xr = *(const f32x4*)xo(0), dr = *(const f32x4*)dof(0);
+        f32x4 xr = *(const f32x4*)xo(0), dr = row_terms(dsum_s, t, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < QB * 4; ++n) {
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
             const f32x4 x = xr, dd = dr;
             if (n + 1 < QB * 4) {
                 xr = *(const f32x4*)xo(n + 1);
-                dr = *(const f32x4*)dof(n + 1);
+                dr = row_terms(dsum_s, t, n + 1);
             }
             float ds[4];
 #pragma unroll
@@ -729,8 +732,9 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
             const int i0 = i_last - t * BQ;
             wait_vmem();
             __syncthreads();
-            // ---- P side: S = Q K^T of tile t
+            // ---- P side: S = Q K^T of tile t (its LSE read meanwhile)
             const FA_LDS char* const qT = qL + (t % NQ) * TILE;
+            f32x4 lreg[QB * 4];
             V8 qa[kPf];
 #pragma unroll
             for (int j = 0; j < kPf; ++j) qa[j] = *(const FA_LDS V8*)(qT + so(j));
@@ -740,6 +744,7 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
                 const int qb = i % QB, c = i / QB;
                 sc[qb] = mfma32(qa[i % kPf], kv[c], c == 0 ? f32x16{} : sc[qb]);
                 if (i + kPf < SI) qa[i % kPf] = *(const FA_LDS V8*)(qT + so(i + kPf));
+                if (i < QB * 4) lreg[i] = row_terms(lse_s, t, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
@@ -755,16 +760,11 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
             }
             // P = exp2(s scale log2(e) - LSE_i log2(e)); P Z' into the dV operands,
             // P (sign = dropped) to the dS side
-            const float* const lse_t = lse_s + (t % NQ) * 64;
             float* const xp = x_s + (t & 1) * XF + pair * QB * 16 * 64;
-            auto lof = [&](int n) { return lse_t + (n >> 2) * 32 + 8 * (n & 3) + 4 * hi; };
-            f32x4 lr = *(const f32x4*)lof(0);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < QB * 4; ++n) {
                 const int qb = n >> 2, g = n & 3;
-                const f32x4 lv = lr;
-                if (n + 1 < QB * 4) lr = *(const f32x4*)lof(n + 1);
+                const f32x4 lv = lreg[n];
                 f32x4 x;
                 const int qc = 2 * qb + (g >> 1), i = 4 * (g & 1);
 #pragma unroll
