@@ -527,8 +527,9 @@ __global__ __launch_bounds__(kNW * 64) void bwd_kv_kernel(BwdParams p) {
     }
 }
 
-// Key-side pass of the two-pass form at d = 64 and 128 with the work of 32
-// keys split between two waves on one SIMD (8 waves, 128 keys per workgroup).
+// Key-side pass of the two-pass form at d = 128 with the work of 32 keys
+// split between two waves on one SIMD (8 waves, 128 keys per workgroup). (It
+// also builds for d = 64, where the one-wave kernel above measured faster.)
 // Wave p (p < 4) takes the P side: S = Q K^T, P = exp(S - LSE), and
 // dV^T += dO^T (P Z'). Wave p + 4, on the same SIMD, takes the dS side:
 // dP = dO V^T, dS = P (dP Z' - D), and dK^T += Q^T dS. Each wave then holds one
