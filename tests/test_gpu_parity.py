@@ -314,6 +314,44 @@ def test_dropout_mask_through_causal_backward_dq(deterministic):
             assert np.array_equal(got[b, h], causal_keep(b, h, rows, cols, w)), (j0, b, h)
 
 
+@pytest.mark.parametrize("deterministic", [False, True], ids=["fused", "two_pass"])
+def test_dropout_mask_through_d128_backward(deterministic):
+    """d = 128, causal, p = 0.1: in the two-pass form the key side is split over two
+    waves per SIMD, one applying Z to P for dV, the other reading Z back from the sign
+    of the P it receives for dS. dO rows i_c = e_c give dV_j[c] = P_{i_c j} Z'_{i_c j}
+    (the first wave's mask); Q rows i_c = e_c with every other Q row 0, V and dO all
+    ones and O = 0 (so D = 0 and dP = d) give dK_j[c] = scale d P_{i_c j} Z'_{i_c j}
+    (the second wave's)."""
+    B, H, N, d, p = 1, 2, 512, 128, 0.1
+    q, k, v = normal_tensors((B, H, N, d), 6262, 3, torch.bfloat16)
+    gk = k.cuda()
+    cols = np.arange(N)
+    for i0 in (0, 200, 384):
+        rows = np.arange(i0, i0 + d)
+        ref = [oracle.keep_mask(0, h, rows, cols, p, SEED) & (cols[None, :] <= rows[:, None]) for h in range(H)]
+        # dV: the P side
+        gq, gv = q.cuda(), v.cuda()
+        _, lse = fa.fwd(gq, gk, gv, causal=True)
+        do = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+        do[:, :, torch.as_tensor(rows), torch.arange(d)] = 1.0
+        _, _, dv = fa.bwd(gq, gk, gv, torch.zeros_like(gq), lse, do.cuda(), causal=True, dropout_p=p,
+                          seed=SEED, deterministic=deterministic)
+        got = dv.float().cpu().numpy() != 0
+        for h in range(H):
+            assert np.array_equal(got[0, h].T, ref[h]), ("dV", i0, h)
+        # dK: the dS side
+        q1 = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+        q1[:, :, torch.as_tensor(rows), torch.arange(d)] = 1.0
+        gq1 = q1.cuda()
+        ones = torch.ones((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        _, lse1 = fa.fwd(gq1, gk, ones, causal=True)
+        _, dk, _ = fa.bwd(gq1, gk, ones, torch.zeros_like(gq1), lse1, ones, causal=True, dropout_p=p,
+                          seed=SEED, deterministic=deterministic)
+        got = dk.float().cpu().numpy() != 0
+        for h in range(H):
+            assert np.array_equal(got[0, h].T, ref[h]), ("dK", i0, h)
+
+
 # ------------------------------------------------------------ other properties
 def test_forward_is_deterministic():
     shape = (2, 4, 1000, 128)
