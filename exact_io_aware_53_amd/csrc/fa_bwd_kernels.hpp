@@ -549,15 +549,16 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
     constexpr int NW = 2 * kNW;                      // waves per workgroup
     constexpr int BQ = 64, QB = 2, CH = D / 8, DB = D / 32, NCD = D / 16;
     constexpr int TILE = BQ * D * 2, ROW = D * 2;
-    constexpr int QLOADS = BQ * CH / (64 * kNW);     // copies per dS-side wave and tensor
+    constexpr int QLOADS = BQ * CH / (64 * kNW);     // copies per P-side wave and tensor
     constexpr int NQ = 3, NO = 2;                    // Q and dO tile buffers
     constexpr int XF = kNW * QB * 16 * 64;           // floats of P per exchange buffer
     constexpr int kPf = FA_KVS_PF, kTf = FA_KVS_TF;
+    constexpr int kXa = 2;                           // dS side: P and D groups read ahead
     constexpr int SI = QB * NCD;                     // score products per wave and tile
     constexpr int TI = (BQ / 16) * DB;               // dV or dK products per wave and tile
     static_assert(D == 64 || D == 128, "d = 64 or 128");
     static_assert(QB * 4 <= SI, "the P side reads its LSE groups during the score products");
-    static_assert(QLOADS >= 1 && QLOADS * 64 * kNW == BQ * CH, "copies split over the dS-side waves");
+    static_assert(QLOADS >= 1 && QLOADS * 64 * kNW == BQ * CH, "copies split over the P-side waves");
     __shared__ __attribute__((aligned(1024))) char q_s[NQ * TILE];
     __shared__ __attribute__((aligned(1024))) char do_s[NO * TILE];
     __shared__ __attribute__((aligned(16))) float x_s[2 * XF];
@@ -635,10 +636,13 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
     f32x16 sc[QB];                  // S (P side) or dP of the previous tile (dS side)
     V8 bop[BQ / 16];                // P Z' (P side) or dS (dS side), bf16 B operands
 
-    // Copies of tile i0: QLOADS Q chunks and QLOADS dO chunks per dS-side wave,
-    // and one row-term copy (LSE by even pairs, D by odd ones).
-    // The dS side issues every copy: it starts each tile with vector work, so
-    // the time the copies take to issue does not hold up the S products.
+    // Copies of tile i0: QLOADS Q chunks and QLOADS dO chunks per P-side wave,
+    // and one row-term copy (LSE by even pairs, D by odd ones). A wave that
+    // issues copies stalls until the CU's memory path has taken them (about
+    // 700 cycles for a tile's 36 KB). The P side issues every copy, after its
+    // score products: its waves wait at each barrier for the dS side, so the
+    // stall comes out of that wait. Issued by the dS side, the copies delayed
+    // its dS elements, which lie on the tile's critical path.
     auto issue_tile = [&](int i0, int t) __attribute__((always_inline)) {
         const int qbuf = t % NQ, obuf = t % NO;
 #pragma unroll
@@ -667,17 +671,22 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
     auto ds_side = [&](int t, auto next, int tn) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
         const float* const xp = x_s + (t & 1) * XF + pair * QB * 16 * 64;
-        // group n: its P and D are read one group ahead
+        // group n: its P and D are read kXa groups ahead
         auto xo = [&](int n) { return xp + (n * 64 + lane) * 4; };
-        f32x4 xr = *(const f32x4*)xo(0), dr = row_terms(dsum_s, t, 0);
+        f32x4 xr[kXa], dr[kXa];
+#pragma unroll
+        for (int a = 0; a < kXa; ++a) {
+            xr[a] = *(const f32x4*)xo(a);
+            dr[a] = row_terms(dsum_s, t, a);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < QB * 4; ++n) {
             const int qb = n >> 2, g = n & 3;
-            const f32x4 x = xr, dd = dr;
-            if (n + 1 < QB * 4) {
-                xr = *(const f32x4*)xo(n + 1);
-                dr = row_terms(dsum_s, t, n + 1);
+            const f32x4 x = xr[n % kXa], dd = dr[n % kXa];
+            if (n + kXa < QB * 4) {
+                xr[n % kXa] = *(const f32x4*)xo(n + kXa);
+                dr[n % kXa] = row_terms(dsum_s, t, n + kXa);
             }
             float ds[4];
 #pragma unroll
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
     const int i_first = CAUSAL ? j0 : 0;
     const int i_last = (N - 1) / BQ * BQ;
     const int ntiles = (i_last - i_first) / BQ + 1;   // tile t starts at row i_last - t BQ
-    if (dside) issue_tile(i_last, 0);
+    if (!dside) issue_tile(i_last, 0);
 
     // Each side runs a loop of its own (their loop-invariant values would
     // otherwise all be live in one loop); both take the same barriers.
@@ -748,6 +757,8 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
                 if (i < QB * 4) lreg[i] = row_terms(lse_s, t, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // the next tile's copies (see issue_tile)
+            if (t + 1 < ntiles) issue_tile(i0 - BQ, t + 1);
             if ((CAUSAL && i0 < kw + 31) || kw + 32 > N || i0 + BQ > N) {
                 const int e_lo = CAUSAL ? my_key - i0 - 4 * hi : -1;   // causal: e >= e_lo
                 const int e_hi = my_key < N ? N - i0 - 4 * hi : 0;       // e < e_hi (none past N)
@@ -804,7 +815,6 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
             const int i0 = i_last - t * BQ;
             wait_vmem();
             __syncthreads();
-            if (t + 1 < ntiles) issue_tile(i0 - BQ, t + 1);
             // ---- dS side: dS and dK of tile t - 1, with the dP products of tile t
             if (t == 0) {
                 const FA_LDS char* const doT = doL;
