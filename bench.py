@@ -251,7 +251,8 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "fwd_kernel",
+                     "traffic": traffic,
+                     "kernel": "fwd_pp_kernel" if w.d == 128 and w.dropout_p == 0.0 else "fwd_kernel",
                      "kernel_ms": round(kern_ms, 4), "ideal_io_bytes": io_bytes},
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "peak_extra_device_bytes": int(peak_extra),

@@ -41,6 +41,9 @@
 //   their sequences along the token dimension (cu_seqlens offsets); a
 //   workgroup whose block lies past its sequence's end returns at once.
 // * Head sizes 32, 64, 96, 128 and 256 (the last with 64-key tiles).
+// * At d = 128 without dropout the 8-wave grid runs fwd_pp_kernel, in which
+//   the two waves of a SIMD alternate: one issues a tile's products while the
+//   other runs its softmax (same arithmetic, same bits).
 #pragma once
 
 #include "fa_device.hpp"
@@ -63,6 +66,10 @@ namespace {
 constexpr float DROPOUT_SLACK = 8.0f;     // log2 units
 
 // LDS operand reads kept in flight ahead of the matrix-core product that uses them.
+// d = 128 without dropout on the 8-wave grid: the two-group kernel (0: fwd_kernel).
+#ifndef FA_FWD_PP
+#define FA_FWD_PP 1
+#endif
 #ifndef FA_FWD_PREFETCH
 #define FA_FWD_PREFETCH 4
 #endif
@@ -410,6 +417,220 @@ void fwd_kernel(FwdParams p) {
     }
 }
 
+// Two-group form of the forward for d = 128 without dropout (same tiles, rows
+// per wave and arithmetic as fwd_kernel, so the same bits): the waves of a
+// SIMD take turns. Waves 0-3 (group 0) issue the products of their rows while
+// waves 4-7 (group 1) compute the softmax of theirs, and the other way round in
+// the next half step; a workgroup barrier separates the half steps. In half
+// step 2k group 0 runs O~ += P(k-1) V(k-1) and S(k) = Q K(k)^T and group 1 the
+// softmax of tile k-1; in half step 2k+1 group 0 runs the softmax of tile k and
+// group 1 the products. One wave then owns the SIMD's matrix core for a whole
+// run of 64 products, and the other wave's exponentials run beside it, where in
+// fwd_kernel both waves' softmax phases overlap for most of their length.
+// Tile copies go out from the group in its softmax half: K(k+1) by group 1 in
+// half step 2k (needed from 2k+2), V(k) by group 0 in half step 2k+1 (needed
+// from 2k+2). Each group waits for its own copies at the start of its next
+// products half.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_pp_kernel(FwdParams p) {
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
+    using V2 = typename Vec<T>::x2;
+    constexpr int BC = 128, NW = 8, WR = 32, BR = NW * WR;
+    constexpr int KB = BC / 32, NC = BC / 16, DB = D / 32;
+    using PT = PaddedTiles<D, BC>;
+    constexpr int K_TILE = PT::K_TILE, V_TILE = PT::V_TILE;
+    constexpr int S_MFMA = KB * (D / 16), PV_MFMA = NC * DB;
+
+    __shared__ __attribute__((aligned(1024))) char kbuf[2 * K_TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf[2 * V_TILE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    int bh, slot;
+    decode_block(blockIdx.x, p.heads, CAUSAL ? (p.nqb + 1) / 2 : p.nqb, false, bh, slot);
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    const int b = bh / p.H, h = bh - b * p.H;
+    int start, N;
+    sequence(p.cu, p.total, p.N, b, start, N);
+    const int nqb = (N + BR - 1) / BR;
+    if (slot >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;
+    const T* const qh = (const T*)p.q + p.lq.base(b, h, start);
+    const T* const kh = (const T*)p.k + p.lk.base(b, h, start);
+    const T* const vh = (const T*)p.v + p.lv.base(b, h, start);
+    T* const oh = (T*)p.o + p.lo.base(b, h, start);
+    float* const lh = p.lse + p.ll.base(b, h, start);
+    const auto rs_q = make_rsrc(qh, (uint32_t)(((size_t)(N - 1) * p.lq.sn + D) * 2));
+    const auto rs_k = make_rsrc(kh, (uint32_t)(((size_t)(N - 1) * p.lk.sn + D) * 2));
+    const auto rs_v = make_rsrc(vh, (uint32_t)(((size_t)(N - 1) * p.lv.sn + D) * 2));
+    const int ldq = p.lq.sn, ldo = p.lo.sn, ldl = p.ll.sn;
+
+    // each group's four waves share the copy blocks of the tensor it copies
+    const TileCopy<D, BC, PT::KCH, 4> kcopy(wave & 3, lane, p.lk.sn);
+    const TileCopy<D, BC, PT::VCH, 4> vcopy(wave & 3, lane, p.lv.sn);
+    const int kbase = k_base<D, BC>(lane), vbase = v_base<D, BC>(lane);
+
+    auto run_block = [&](int qb) {
+        const int q0 = qb * BR;
+        const int qw = q0 + wave * WR;
+        const int my_q = qw + l32;
+        V8 qreg[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            qreg[c] = __builtin_bit_cast(V8, buffer_load16(rs_q, (uint32_t)(my_q * ldq + 16 * c + 8 * hi) * 2));
+        f32x16 oacc[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+        float m2 = -INFINITY, lsum = 0.0f;
+
+        const int last_q = min(N, q0 + BR) - 1;
+        const int ntiles = CAUSAL ? (last_q / BC + 1) : (N + BC - 1) / BC;
+        const int ntiles_w = qw >= N ? 0 : CAUSAL ? min(ntiles, min(qw + WR - 1, N - 1) / BC + 1) : ntiles;
+
+        f32x16 s[KB];
+        V8 pb[NC];
+        // S^T = K Q^T over K tile t
+        auto s_products = [&](int t) __attribute__((always_inline)) {
+            const FA_LDS char* kt = (const FA_LDS char*)kbuf + (t & 1) * K_TILE;
+            V8 kop[kPrefetch];
+#pragma unroll
+            for (int j = 0; j < kPrefetch; ++j) kop[j] = k_operand<D, BC, V8>(kt, kbase, j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < S_MFMA; ++i) {
+                const int kb = i % KB, c = i / KB;
+                s[kb] = mfma32(kop[i % kPrefetch], qreg[c], c == 0 ? f32x16{} : s[kb]);
+                if (i + kPrefetch < S_MFMA) kop[i % kPrefetch] = k_operand<D, BC, V8>(kt, kbase, i + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // O~^T += V^T P^T over V tile t
+        auto pv_products = [&](int t) __attribute__((always_inline)) {
+            const FA_LDS char* vt = (const FA_LDS char*)vbuf + (t & 1) * V_TILE;
+            V8 vop[kPrefetch];
+#pragma unroll
+            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC, V8>(vt, vbase, j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < PV_MFMA; ++j) {
+                oacc[j % DB] = mfma32(vop[j % kPrefetch], pb[j / DB], oacc[j % DB]);
+                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC, V8>(vt, vbase, j + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // mask, exact running maximum (rescaling l and O~ when it grows), and
+        // P~ = exp2(s c - m2) into pb, as in fwd_kernel without dropout
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            const int k0 = t * BC;
+            if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N)) {
+                const int rel = (CAUSAL ? min(my_q, N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) > rel ? -INFINITY : s[kb][r];
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            const float mxc = max_with_partner32(mx) * p.sl2;
+            if (__builtin_amdgcn_ballot_w64(mxc > m2)) {
+                const float m_new = fmaxf(m2, mxc);
+                const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m2 - m_new);
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m2 = m_new;
+            }
+            const float neg = -m2;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float x0 = fast_exp2(fmaf(s[kb][r], p.sl2, neg));
+                    const float x1 = fast_exp2(fmaf(s[kb][r + 1], p.sl2, neg));
+                    lsum += x0;
+                    lsum += x1;
+                    const int pc = kb * 2 + r / 8, pi = r % 8;
+                    pb[pc][pi] = (T)x0;
+                    pb[pc][pi + 1] = (T)x1;
+                }
+        };
+        auto copy_k = [&](int t) __attribute__((always_inline)) {
+            kcopy.issue(rs_k, (FA_LDS char*)kbuf + (t & 1) * K_TILE, t, wave & 3);
+        };
+        auto copy_v = [&](int t) __attribute__((always_inline)) {
+            vcopy.issue(rs_v, (FA_LDS char*)vbuf + (t & 1) * V_TILE, t, wave & 3);
+        };
+
+        // Half steps 0 .. 2 ntiles + 1; each group runs a loop of its own with
+        // the same barriers.
+        if (grp == 0) {
+            for (int k = 0; k <= ntiles; ++k) {
+                wait_vmem();                  // V(k-1), issued in half step 2k-1
+                __syncthreads();              // half step 2k: products
+                if (k >= 1 && k - 1 < ntiles_w) pv_products(k - 1);
+                if (k < ntiles_w) s_products(k);
+                __syncthreads();              // half step 2k+1: softmax
+                if (k < ntiles) copy_v(k);
+                if (k < ntiles_w) softmax(k);
+            }
+        } else {
+            copy_k(0);
+            for (int k = 0; k <= ntiles; ++k) {
+                wait_vmem();                  // K(k), issued in half step 2k-2
+                __syncthreads();              // half step 2k: softmax
+                if (k + 1 < ntiles) copy_k(k + 1);
+                if (k >= 1 && k - 1 < ntiles_w) softmax(k - 1);
+                __syncthreads();              // half step 2k+1: products
+                if (k >= 1 && k - 1 < ntiles_w) pv_products(k - 1);
+                if (k < ntiles_w) s_products(k);
+            }
+        }
+
+        // epilogue: O = O~ / l, LSE = (m2 + log2 l) ln 2
+        const float ltot = add_with_partner32(lsum);
+        const float inv = 1.0f / ltot;
+        if (my_q < N) {
+            T* orow = oh + (size_t)my_q * ldo;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[db][4 * g + i] * inv);
+                    *(V4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
+                }
+            if (hi == 0) lh[(size_t)my_q * ldl] = (m2 + fast_log2(ltot)) * kLn2;
+        }
+    };
+
+    if (CAUSAL) {
+        const int longer = nqb - 1 - slot;
+        run_block(longer);
+        if (slot != longer) {
+            wait_vmem();
+            __syncthreads();     // every wave is done with the buffers the next block refills
+            run_block(slot);
+        }
+    } else {
+        run_block(slot);
+    }
+}
+
 // Keys per K/V tile and waves (32 query rows each) per workgroup: 128-key tiles
 // and 8 waves, one workgroup per CU (two waves per SIMD) sharing each K/V copy.
 // d = 256 takes 64-key tiles (two 128-key K/V tiles would not fit in LDS) and
@@ -469,8 +690,11 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
     p.thr = dropout_threshold(a.s.dropout_p);
     p.key = PhiloxKey{(uint32_t)(a.s.seed & 0xffffffffu), (uint32_t)(a.s.seed >> 32)};
     const int blocks = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * blocks),
-                       dim3(NW * 64), 0, st, p);
+    if constexpr (FA_FWD_PP && D == 128 && BC == 128 && NW == 8 && RB == 1 && !DROPOUT)
+        hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL>), dim3(p.heads * blocks), dim3(NW * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, RB, CAUSAL, DROPOUT>), dim3(p.heads * blocks),
+                           dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 

@@ -460,6 +460,27 @@ def test_forward_eight_wave_grids(shape, causal, p):
                         tag=f"8-wave forward {shape} causal={causal} p={p}")
 
 
+# d = 128 without dropout on the 8-wave grid runs the two-group forward (waves
+# 0-3 and 4-7 alternate products and softmax half steps). B*H = 80 heads of
+# N = 1000 give 160 causal workgroups (more than the 4-wave grid can fit in
+# one round), four 128-key tiles per 256-row block, a ragged last tile and
+# causal block pairs of unequal length; Q x 16 drives the rescale path.
+TWO_GROUP = [(1, 80, 1000, 128, True, 1.0), (1, 80, 1000, 128, False, 1.0),
+             (1, 80, 1000, 128, True, 16.0), (2, 40, 777, 128, False, 16.0)]
+
+
+@pytest.mark.parametrize("case", TWO_GROUP, ids=lambda c: "x".join(map(str, c[:4])) + f"-causal{int(c[4])}-q{c[5]:g}")
+def test_forward_two_group_kernel(case):
+    B, H, N, d, causal, qmul = case
+    q, k, v = normal_tensors((B, H, N, d), 6100 + N + int(qmul), 3, torch.bfloat16)
+    q = (q.float() * qmul).to(torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=0.0, seed=SEED)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 7), (0, 38), (B - 1, H - 1)]
+    check_forward_heads(q, k, v, o, lse, causal, 0.0, SEED, TOL["bf16"], heads,
+                        tag=f"two-group forward {case}", wide_scores=qmul > 1.0)
+
+
 def test_forward_four_wave_grid_at_the_limit():
     """B1 H16 N4096 d128 causal: 16 heads x 16 pairs of 128-row blocks = 256
     workgroups, the largest grid that takes the 4-wave kernel."""
