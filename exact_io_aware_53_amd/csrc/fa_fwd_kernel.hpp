@@ -440,8 +440,14 @@ void fwd_pp_kernel(FwdParams p) {
     constexpr int BC = 128, NW = 8, WR = 32, BR = NW * WR;
     constexpr int KB = BC / 32, NC = BC / 16, DB = D / 32;
     using PT = PaddedTiles<D, BC>;
-    constexpr int K_TILE = PT::K_TILE, V_TILE = PT::V_TILE;
+    // K rows padded as in fwd_kernel. V rows unpadded: the 64-byte segment s of
+    // tile row r sits at segment s ^ (r & 3), so the four rows of a transposed
+    // read pass still fall on four distinct 64-byte bank groups, a tile is 32
+    // copy blocks instead of 40, and a lane's copy offset is one register.
+    constexpr int VROW = D * 2;
+    constexpr int K_TILE = PT::K_TILE, V_TILE = BC * VROW;
     constexpr int S_MFMA = KB * (D / 16), PV_MFMA = NC * DB;
+    static_assert(D == 128, "the swizzle assumes four 64-byte segments per row");
 
     __shared__ __attribute__((aligned(1024))) char kbuf[2 * K_TILE];
     __shared__ __attribute__((aligned(1024))) char vbuf[2 * V_TILE];
@@ -473,8 +479,16 @@ void fwd_pp_kernel(FwdParams p) {
 
     // each group's four waves share the copy blocks of the tensor it copies
     const TileCopy<D, BC, PT::KCH, 4> kcopy(wave & 3, lane, p.lk.sn);
-    const TileCopy<D, BC, PT::VCH, 4> vcopy(wave & 3, lane, p.lv.sn);
-    const int kbase = k_base<D, BC>(lane), vbase = v_base<D, BC>(lane);
+    const int kbase = k_base<D, BC>(lane);
+    // swizzled V: the lane's read base for d block 0 (d block db is at base ^
+    // 64 db: the segment bits 6-7 are the only ones the swizzle touches), and
+    // its source offset in a 1 KB copy block (4 rows; lane -> row lane/16,
+    // chunk lane%16)
+    const int vsw0 = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VROW + 64 * ((lane >> 2) & 3) +
+                     2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const uint32_t vcopy_lane =
+        (uint32_t)((lane >> 4) * p.lv.sn + (((lane & 15) ^ (((lane >> 4) & 3) << 2)) * 8)) * 2;
+    constexpr int VBLKS = V_TILE / 1024 / 4;   // copy blocks per group-0 wave and tile
 
     auto run_block = [&](int qb) {
         const int q0 = qb * BR;
@@ -497,6 +511,13 @@ void fwd_pp_kernel(FwdParams p) {
 
         f32x16 s[KB];
         V8 pb[NC];
+        // block i of group 0's share of V tile t (rows 4 blk .. 4 blk + 3)
+        auto copy_v_blk = [&](int t, int i) __attribute__((always_inline)) {
+            const int blk = i * 4 + (wave & 3);
+            const uint32_t base = (uint32_t)((t * BC + blk * 4) * p.lv.sn) * 2;
+            buffer_to_lds16_async(rs_v, (FA_LDS void*)((FA_LDS char*)vbuf + (t & 1) * V_TILE + blk * 1024),
+                                  vcopy_lane + (uint32_t)__builtin_amdgcn_readfirstlane(base));
+        };
         // S^T = K Q^T over K tile t
         auto s_products = [&](int t) __attribute__((always_inline)) {
             const FA_LDS char* kt = (const FA_LDS char*)kbuf + (t & 1) * K_TILE;
@@ -512,17 +533,32 @@ void fwd_pp_kernel(FwdParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // V^T operand j = c * DB + db (16-key chunk c, d block db) from the
+        // swizzled tile, read base vb
+        auto v_op = [&](const FA_LDS char* vt, int vb, int j) __attribute__((always_inline)) {
+            s16x4 x[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                x[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (FA_LDS s16x4*)(vt + (vb ^ (64 * (j % DB))) + (16 * (j / DB) + 8 * half) * VROW));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            return __builtin_bit_cast(V8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
         // O~^T += V^T P^T over V tile t
         auto pv_products = [&](int t) __attribute__((always_inline)) {
             const FA_LDS char* vt = (const FA_LDS char*)vbuf + (t & 1) * V_TILE;
+            // an opaque copy of the read base: its four d-block variants are then
+            // formed here, not kept live across the whole loop
+            int vb = vsw0;
+            asm volatile("" : "+v"(vb));
             V8 vop[kPrefetch];
 #pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_operand<D, BC, V8>(vt, vbase, j);
+            for (int j = 0; j < kPrefetch; ++j) vop[j] = v_op(vt, vb, j);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < PV_MFMA; ++j) {
                 oacc[j % DB] = mfma32(vop[j % kPrefetch], pb[j / DB], oacc[j % DB]);
-                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_operand<D, BC, V8>(vt, vbase, j + kPrefetch);
+                if (j + kPrefetch < PV_MFMA) vop[j % kPrefetch] = v_op(vt, vb, j + kPrefetch);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -571,9 +607,6 @@ void fwd_pp_kernel(FwdParams p) {
         auto copy_k = [&](int t) __attribute__((always_inline)) {
             kcopy.issue(rs_k, (FA_LDS char*)kbuf + (t & 1) * K_TILE, t, wave & 3);
         };
-        auto copy_v = [&](int t) __attribute__((always_inline)) {
-            vcopy.issue(rs_v, (FA_LDS char*)vbuf + (t & 1) * V_TILE, t, wave & 3);
-        };
 
         // Half steps 0 .. 2 ntiles + 1; each group runs a loop of its own with
         // the same barriers.
@@ -583,8 +616,11 @@ void fwd_pp_kernel(FwdParams p) {
                 __syncthreads();              // half step 2k: products
                 if (k >= 1 && k - 1 < ntiles_w) pv_products(k - 1);
                 if (k < ntiles_w) s_products(k);
-                __syncthreads();              // half step 2k+1: softmax
-                if (k < ntiles) copy_v(k);
+                __syncthreads();              // half step 2k+1: softmax, after the copies of V(k)
+                if (k < ntiles) {
+#pragma unroll
+                    for (int i = 0; i < VBLKS; ++i) copy_v_blk(k, i);
+                }
                 if (k < ntiles_w) softmax(k);
             }
         } else {
