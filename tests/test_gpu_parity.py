@@ -481,6 +481,24 @@ def test_forward_two_group_kernel(case):
                         tag=f"two-group forward {case}", wide_scores=qmul > 1.0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("qmul", [1.0, 16.0])
+def test_two_group_forward_bitwise_equal_to_one_group(causal, qmul):
+    """Each row's arithmetic is the same in both forward kernels, so two heads
+    computed in an 80-head grid (the two-group kernel) and on their own (a grid
+    small enough for the 4-wave one-group kernel) give the same bits."""
+    B, H, N, d = 1, 80, 1000, 128
+    q, k, v = normal_tensors((B, H, N, d), 6200 + int(qmul), 3, torch.bfloat16)
+    q = (q.float() * qmul).to(torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=0.0, seed=SEED)
+    heads = [3, 41]
+    sub = [t[:, heads].contiguous() for t in (q, k, v)]
+    o2, lse2 = fa.fwd(*upload(sub), causal=causal, dropout_p=0.0, seed=SEED)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, heads].cpu(), o2.cpu())
+    assert torch.equal(lse[:, heads].cpu(), lse2.cpu())
+
+
 def test_forward_four_wave_grid_at_the_limit():
     """B1 H16 N4096 d128 causal: 16 heads x 16 pairs of 128-row blocks = 256
     workgroups, the largest grid that takes the 4-wave kernel."""
