@@ -383,6 +383,42 @@ void fwd_kernel(FwdParams p) {
         }
 
         // ---- epilogue: O = O~ / (l (1 - p)) (lb with dropout), LSE = (m2 + log2 l) ln 2
+        // Where the buffers allow, the wave's rows of O go through LDS so that
+        // each store writes four whole rows (a lane of the product layout holds
+        // 4-element runs of one row: its stores would touch 32 rows each). The
+        // K and V buffers not used by the last tile are free for every wave
+        // since that tile's barrier: the first half of the waves stages in the
+        // K one, the second half in the V one, 32 rows of 2d + 16 bytes each
+        // (the pad keeps the row writes of the 32 lanes on distinct bank pairs).
+        constexpr int SROW = D * 2 + 16, STG = 32 * SROW;
+        constexpr bool STAGE = RB == 1 && D % 64 == 0 && (NW / 2) * STG <= K_TILE && (NW / 2) * STG <= V_TILE;
+        if constexpr (STAGE) {
+            const int fb = ntiles & 1;                 // the buffer of tile ntiles - 2
+            FA_LDS char* const stg = (wave < NW / 2 ? (FA_LDS char*)kbuf + fb * K_TILE
+                                                    : (FA_LDS char*)vbuf + fb * V_TILE) + (wave % (NW / 2)) * STG;
+            const float ltot = add_with_partner32(lsum[0]);
+            const float lbtot = DROPOUT ? add_with_partner32(lbf[0]) : ltot;
+            const float inv = p.inv_keep / lbtot;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[0][db][4 * g + i] * inv);
+                    *(FA_LDS V4*)(stg + l32 * SROW + (32 * db + 8 * g + 4 * hi) * 2) = w;
+                }
+            asm volatile("" ::: "memory");
+            constexpr int RCH = D / 8;               // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < 32 * RCH / 64; ++i) {
+                const int pos = i * 64 + lane, r = pos / RCH, c = pos % RCH;
+                const V8 w = *(const FA_LDS V8*)(stg + r * SROW + c * 16);
+                if (qw + r < N) *(V8*)(oh + (size_t)(qw + r) * ldo + c * 8) = w;
+            }
+            const int my_q = qw + l32;
+            if (hi == 0 && my_q < N) lh[(size_t)my_q * ldl] = (m2[0] + fast_log2(ltot)) * kLn2;
+        } else
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int my_q = qw + 32 * rb + l32;
@@ -639,19 +675,32 @@ void fwd_pp_kernel(FwdParams p) {
         // epilogue: O = O~ / l, LSE = (m2 + log2 l) ln 2
         const float ltot = add_with_partner32(lsum);
         const float inv = 1.0f / ltot;
-        if (my_q < N) {
-            T* orow = oh + (size_t)my_q * ldo;
+        // The wave's 32 rows of O go through LDS so that each store writes
+        // four whole rows (a lane of the product layout holds 4-element runs
+        // of one row: its stores would touch 32 rows each). No K tile is
+        // read any more: group g stages in the g-th half of the K buffers,
+        // wave w in its own 32 rows of 272 bytes (16 bytes of pad keep the
+        // row writes of the 32 lanes on distinct bank pairs).
+        constexpr int SROW = D * 2 + 16;
+        static_assert(8 * 32 * SROW <= 2 * K_TILE, "staging fits in the K buffers");
+        FA_LDS char* const stg = (FA_LDS char*)kbuf + (grp * 4 + (wave & 3)) * (32 * SROW);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    V4 w;
+            for (int g = 0; g < 4; ++g) {
+                V4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[db][4 * g + i] * inv);
-                    *(V4*)(orow + 32 * db + 8 * g + 4 * hi) = w;
-                }
-            if (hi == 0) lh[(size_t)my_q * ldl] = (m2 + fast_log2(ltot)) * kLn2;
+                for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[db][4 * g + i] * inv);
+                *(FA_LDS V4*)(stg + l32 * SROW + (32 * db + 8 * g + 4 * hi) * 2) = w;
+            }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 32 * D * 2 / 1024; ++i) {
+            const int r = 4 * i + (lane >> 4), c = lane & 15;
+            const V8 w = *(const FA_LDS V8*)(stg + r * SROW + c * 16);
+            if (qw + r < N) *(V8*)(oh + (size_t)(qw + r) * ldo + c * 8) = w;
         }
+        if (hi == 0 && my_q < N) lh[(size_t)my_q * ldl] = (m2 + fast_log2(ltot)) * kLn2;
     };
 
     if (CAUSAL) {
