@@ -838,21 +838,36 @@ __global__ __launch_bounds__(2 * kNW * 64) void bwd_kv_split_kernel(BwdParams p)
         ds_side(ntiles - 1, std::false_type{}, 0);
     }
 
-    if (my_key < N) {
+    {
+        // dV (P side) or dK (dS side) through LDS, stored four whole rows per
+        // instruction (a lane of the product layout holds 4-element runs of one
+        // key's row, so its direct stores touch 32 rows each). The P side stages
+        // in the dO buffers (past the final barrier nothing reads them), the dS
+        // side in the exchange buffer its last dS did not read; 8 KB per wave,
+        // rows unpadded with 16-byte chunk c of row r at c ^ (r % RCH).
         using V4 = typename Vec<T>::x4;
-        const Strides& lo = dside ? p.ldk : p.ldv;
-        T* row = (T*)(dside ? p.dk : p.dv) + lo.base(b, h, start) + (size_t)my_key * lo.sn;
+        constexpr int RCH = D / 8, SROWB = D * 2;
+        static_assert(kNW * 32 * SROWB <= NO * TILE && kNW * 32 * SROWB <= XF * 4, "staging fits");
+        FA_LDS char* const stg = (dside ? (FA_LDS char*)(x_s + (ntiles & 1) * XF) : doL) + pair * (32 * SROWB);
         const float mul = dside ? p.scale : 1.0f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            if (32 * db >= DH) break;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 V4 w;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = (T)(dside ? acc[db][4 * g + i] * mul : acc[db][4 * g + i]);
-                *(V4*)(row + 32 * db + 8 * g + 4 * hi) = w;
+                const int c = 4 * db + g;   // 16-byte chunk of the row (8 elements)
+                *(FA_LDS V4*)(stg + l32 * SROWB + ((c ^ (l32 % RCH)) * 16) + hi * 8) = w;
             }
+        asm volatile("" ::: "memory");
+        const Strides& lo = dside ? p.ldk : p.ldv;
+        T* const base = (T*)(dside ? p.dk : p.dv) + lo.base(b, h, start);
+#pragma unroll
+        for (int i = 0; i < 32 * RCH / 64; ++i) {
+            const int pos = i * 64 + lane, r = pos / RCH, c = pos % RCH;
+            const typename Vec<T>::x8 w = *(const FA_LDS typename Vec<T>::x8*)(stg + r * SROWB + ((c ^ (r % RCH)) * 16));
+            if (kw + r < N && c * 8 < DH) *(typename Vec<T>::x8*)(base + (size_t)(kw + r) * lo.sn + c * 8) = w;
         }
     }
 }
