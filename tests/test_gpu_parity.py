@@ -481,6 +481,20 @@ def test_forward_two_group_kernel(case):
                         tag=f"two-group forward {case}", wide_scores=qmul > 1.0)
 
 
+# Very short sequences over many heads still take the 8-wave grid (640 heads,
+# so the 4-wave grid would not fit one round): one key tile, most waves own
+# only rows past N and skip every tile.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33])
+def test_two_group_forward_short_sequences(N, causal):
+    B, H, d = 1, 640, 128
+    q, k, v = normal_tensors((B, H, N, d), 6300 + N, 3, torch.bfloat16)
+    o, lse = fa.fwd(*upload((q, k, v)), causal=causal, dropout_p=0.0, seed=SEED)
+    torch.cuda.synchronize()
+    check_forward_heads(q, k, v, o, lse, causal, 0.0, SEED, TOL["bf16"], [(0, 0), (0, 255), (0, 639)],
+                        tag=f"two-group forward short N={N} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("qmul", [1.0, 16.0])
 def test_two_group_forward_bitwise_equal_to_one_group(causal, qmul):
